@@ -1,0 +1,97 @@
+"""The CPU oracle against its pins (no GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention, attention_dense, attention_probs, attention_tiled, attention_varlen
+from tests.oracle_pins import ALL_PINS
+
+
+def _tiled_fn(q, k, v, scale, causal):
+    return attention_tiled(q, k, v, scale, causal, block_rows=4, block_cols=3)
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_definition_pins(pin):
+    pin(attention)
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_tiled_pins(pin):
+    """The blockwise algorithm meets the same pins on its own."""
+    pin(_tiled_fn)
+
+
+def test_probs_match_attention_weights():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((9, 4))
+    k = rng.standard_normal((9, 4))
+    for causal in (False, True):
+        P = attention_probs(q, k, 0.5, causal)
+        O, _ = attention(q, k, np.eye(9), 0.5, causal)
+        np.testing.assert_allclose(P, O, atol=1e-14)
+        np.testing.assert_allclose(P.sum(1), 1.0, atol=1e-14)
+
+
+def test_rows_subset_is_a_slice():
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((40, 8)) for _ in range(3))
+    rows = [0, 3, 17, 39]
+    for causal in (False, True):
+        O, L = attention(q, k, v, 0.3, causal)
+        Os, Ls = attention(q, k, v, 0.3, causal, rows=rows)
+        np.testing.assert_array_equal(Os, O[rows])
+        np.testing.assert_array_equal(Ls, L[rows])
+
+
+def test_dense_loops_heads_and_batches():
+    rng = np.random.default_rng(7)
+    B, N, H, d = 2, 12, 3, 4
+    q, k, v = (rng.standard_normal((B, N, H, d)) for _ in range(3))
+    O, L = attention_dense(q, k, v, 0.5, True)
+    assert O.shape == (B, N, H, d) and L.shape == (B, H, N)
+    for b in range(B):
+        for h in range(H):
+            o, l = attention(q[b, :, h], k[b, :, h], v[b, :, h], 0.5, True)
+            np.testing.assert_array_equal(O[b, :, h], o)
+            np.testing.assert_array_equal(L[b, h], l)
+    Os, Ls = attention_dense(q, k, v, 0.5, True, batches=[1], heads=[2], rows=[0, 5])
+    np.testing.assert_array_equal(Os[0, :, 0], O[1, [0, 5], 2])
+    np.testing.assert_array_equal(Ls[0, 0], L[1, 2, [0, 5]])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_per_sequence(causal):
+    """Packing sequences gives the same O and L as running each one alone."""
+    rng = np.random.default_rng(8)
+    lengths = [5, 0, 1, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 2, 4
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    O, L = attention_varlen(q, k, v, cu, 0.6, causal)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    for s, n in enumerate(lengths):
+        a = int(cu[s])
+        if n == 0:
+            continue
+        for h in range(H):
+            o, l = attention(q[a:a + n, h], k[a:a + n, h], v[a:a + n, h], 0.6, causal)
+            np.testing.assert_array_equal(O[a:a + n, h], o)
+            np.testing.assert_array_equal(L[h, a:a + n], l)
+    # and no attention across the boundary: changing another sequence changes nothing
+    k2 = k.copy()
+    k2[cu[3]:cu[4]] += 10.0
+    O2, L2 = attention_varlen(q, k2, v, cu, 0.6, causal)
+    np.testing.assert_array_equal(O2[: cu[3]], O[: cu[3]])
+    np.testing.assert_array_equal(L2[:, : cu[3]], L[:, : cu[3]])
+
+
+def test_causal_requires_square():
+    with pytest.raises(ValueError):
+        attention(np.zeros((3, 2)), np.zeros((4, 2)), np.zeros((4, 2)), 1.0, True)
+
+
+def test_empty_query():
+    O, L = attention(np.zeros((0, 4)), np.zeros((3, 4)), np.zeros((3, 4)), 1.0, False)
+    assert O.shape == (0, 4) and L.shape == (0,)

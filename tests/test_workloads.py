@@ -1,0 +1,68 @@
+"""Seeded input generators (no GPU)."""
+import numpy as np
+import pytest
+
+import workloads as W
+
+
+def test_bf16_rne_hand_picked():
+    f = np.array([
+        1.0,                      # exact
+        1.0 + 2.0**-8,            # halfway between 1.0 and 1+2^-7 -> even (1.0)
+        1.0 + 3 * 2.0**-8,        # halfway between 1+2^-7 and 1+2^-6 -> even (1+2^-6)
+        1.0 + 2.0**-8 + 2.0**-20, # just above halfway -> up
+        -2.5,                     # exact
+        3.0e38,                   # large finite
+        1e-40,                    # float32 subnormal
+        0.0, -0.0,
+    ], dtype=np.float32)
+    bits = W.f32_to_bf16_bits(f)
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020,
+                             0x7F62, 0x0001, 0x0000, 0x8000]
+
+
+def test_bf16_matches_torch_conversion():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    ours = W.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, theirs)
+    back = W.bf16_bits_to_f32(ours)
+    np.testing.assert_array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_dense_is_deterministic_and_shaped():
+    a = W.make_dense(2, 5, 3, 8, seed=9)
+    b = W.make_dense(2, 5, 3, 8, seed=9)
+    for x, y in zip(a, b):
+        assert x.dtype == np.uint16 and x.shape == (2, 5, 3, 8)
+        np.testing.assert_array_equal(x, y)
+    c = W.make_dense(2, 5, 3, 8, seed=10)
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_rms_normalised_rows():
+    q, k, v = W.make_dense(1, 50, 2, 128, seed=3, rms_qk=True)
+    for x in (q, k):
+        ms = np.mean(W.bf16_bits_to_f32(x).astype(np.float64) ** 2, axis=-1)
+        np.testing.assert_allclose(ms, 1.0, atol=2e-2)
+    msv = np.mean(W.bf16_bits_to_f32(v).astype(np.float64) ** 2, axis=-1)
+    assert np.std(msv) > 0.01   # V is not normalised
+
+
+def test_varlen_recipe():
+    w = W.make_workload("varlen")
+    lengths, cu = w["lengths"], w["cu_seqlens"]
+    assert len(lengths) == 64 and lengths.min() >= 256 and lengths.max() <= 1025
+    assert cu.dtype == np.int32 and cu[0] == 0
+    np.testing.assert_array_equal(np.diff(cu), lengths)
+    assert w["q"].shape == (int(cu[-1]), 25, 128)
+    assert w["max_seqlen"] == lengths.max()
+    np.testing.assert_array_equal(lengths, W.varlen_lengths(64, 256, 1025, 4))
+
+
+def test_flop_formulas():
+    assert W.WORKLOADS["prefill8k"].flops() == pytest.approx(2 * 8192**2 * 128 * 32)
+    assert W.WORKLOADS["vit"].flops() == pytest.approx(4 * 1025**2 * 128 * 25 * 32)
+    assert W.varlen_flops([2, 3], 4, 8, False) == 4 * 8 * 4 * 13

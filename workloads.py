@@ -1,0 +1,194 @@
+"""Seeded synthetic workloads for the attention forward pass.
+
+This module only makes inputs. It holds none of the attention arithmetic, and
+it is the one piece of code that both the CPU oracle's tests and the GPU path
+read from. Everything is numpy, so importing it never touches a GPU.
+
+Workloads (shapes follow the pages' models):
+  tiny        B=1  H=2  N=128  d=64   non-causal            seed 1
+  det1600     B=16 H=4  N=1600 d=32   non-causal (40x40 map) seed 2
+  det400      B=16 H=4  N=400  d=32   non-causal (20x20 map) seed 22
+  vit         B=32 H=25 N=1025 d=128  non-causal, Q,K RMS-normalised  seed 3
+  varlen      64 sequences, lengths ~U{256..1025}, H=25 d=128, non-causal  seed 4
+  prefill8k   B=1  H=32 N=8192 d=128  causal                 seed 5
+  prefill2k   B=4  H=32 N=2048 d=128  causal                 seed 55
+
+The detector token counts (40x40, 20x20 and the 4-head, 32-wide head split)
+come from "YOLOv12官版镜像集成Flash Attention v2，提速原理浅析" (sections 2.1 and
+2.3). The ViT shape (448 px / 14 px patches = 32x32 patches + CLS = 1025
+tokens, 25 heads of hidden 3200, bf16, RMSNorm on Q and K) comes from
+"InternViT-6B-448px-V1-2 如何加速注意力计算" (sections 先认识模型 and
+模型侧的启用与降级机制).
+
+Recipe for every draw: numpy.random.default_rng(seed); float32
+standard_normal in C order, drawn in the order lengths (varlen only) -> Q ->
+K -> V; then rounded to bfloat16 with round-to-nearest-even. For "vit", Q and
+K are RMS-normalised over d in float32 (eps 1e-6, unit weight) before the
+rounding; V is not.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 <-> float32, as bit patterns (uint16), by integer arithmetic.
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as uint16. NaN inputs map to a quiet NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        rounded = rounded.copy()
+        rounded[nan] = 0x7FC0
+    return rounded
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _rms_normalise(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(mean(x^2 over the last axis) + eps), in float32, weight 1."""
+    ms = np.mean(x * x, axis=-1, keepdims=True, dtype=np.float32)
+    return (x / np.sqrt(ms + np.float32(eps))).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Workload descriptions
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Dense:
+    """Equal-length batch: Q,K,V,O laid out (B, N, H, d); L laid out (B, H, N)."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    seed: int
+    rms_qk: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        f = 4.0 * self.N * self.N * self.d * self.H * self.B
+        return f / 2 if self.causal else f
+
+    def bytes_compulsory(self) -> int:
+        qkvo = 4 * self.B * self.N * self.H * self.d * 2
+        return qkvo + self.B * self.H * self.N * 4
+
+
+@dataclasses.dataclass(frozen=True)
+class Varlen:
+    """Packed unpadded batch: Q,K,V,O laid out (total, H, d); L laid out (H, total)."""
+    name: str
+    num_seqs: int
+    len_lo: int
+    len_hi: int          # inclusive
+    H: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+WORKLOADS = {
+    "tiny": Dense("tiny", B=1, H=2, N=128, d=64, causal=False, seed=1),
+    "det1600": Dense("det1600", B=16, H=4, N=1600, d=32, causal=False, seed=2),
+    "det400": Dense("det400", B=16, H=4, N=400, d=32, causal=False, seed=22),
+    "vit": Dense("vit", B=32, H=25, N=1025, d=128, causal=False, seed=3, rms_qk=True),
+    "varlen": Varlen("varlen", num_seqs=64, len_lo=256, len_hi=1025, H=25, d=128,
+                     causal=False, seed=4),
+    "prefill8k": Dense("prefill8k", B=1, H=32, N=8192, d=128, causal=True, seed=5),
+    "prefill2k": Dense("prefill2k", B=4, H=32, N=2048, d=128, causal=True, seed=55),
+}
+
+
+def _draw(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def make_dense(B: int, N: int, H: int, d: int, seed: int, rms_qk: bool = False,
+               Nk: int | None = None):
+    """Return (q, k, v) as uint16 bf16 bit patterns, q (B,N,H,d), k/v (B,Nk,H,d)."""
+    Nk = N if Nk is None else Nk
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (B, N, H, d))
+    k = _draw(rng, (B, Nk, H, d))
+    v = _draw(rng, (B, Nk, H, d))
+    if rms_qk:
+        q = _rms_normalise(q)
+        k = _rms_normalise(k)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def varlen_lengths(num_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Integer lengths drawn uniformly from [lo, hi] inclusive (the first draw)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=num_seqs).astype(np.int64)
+
+
+def cu_seqlens_from_lengths(lengths) -> np.ndarray:
+    """Prefix sums [0, n0, n0+n1, ...] as int32."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    assert cu[-1] < 2**31
+    return cu.astype(np.int32)
+
+
+def make_varlen(lengths, H: int, d: int, seed: int, rng: np.random.Generator | None = None):
+    """Return (q, k, v, cu_seqlens): q/k/v (total,H,d) bf16 bits, cu int32."""
+    cu = cu_seqlens_from_lengths(lengths)
+    total = int(cu[-1])
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    q = _draw(rng, (total, H, d))
+    k = _draw(rng, (total, H, d))
+    v = _draw(rng, (total, H, d))
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v), cu
+
+
+def make_workload(name: str):
+    """Materialise a named workload.
+
+    Dense -> dict(q, k, v, scale, causal, shape=(B,N,H,d)).
+    Varlen -> dict(q, k, v, cu_seqlens, max_seqlen, scale, causal, lengths).
+    """
+    w = WORKLOADS[name]
+    if isinstance(w, Dense):
+        q, k, v = make_dense(w.B, w.N, w.H, w.d, w.seed, rms_qk=w.rms_qk)
+        return dict(q=q, k=k, v=v, scale=w.scale, causal=w.causal,
+                    shape=(w.B, w.N, w.H, w.d), spec=w)
+    rng = np.random.default_rng(w.seed)
+    lengths = rng.integers(w.len_lo, w.len_hi + 1, size=w.num_seqs).astype(np.int64)
+    q, k, v, cu = make_varlen(lengths, w.H, w.d, w.seed, rng=rng)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, max_seqlen=int(lengths.max()),
+                scale=w.scale, causal=w.causal, lengths=lengths, spec=w)
+
+
+def varlen_flops(lengths, H: int, d: int, causal: bool) -> float:
+    """4 * d * H * sum(n_i^2), halved when causal."""
+    s = float(np.sum(np.asarray(lengths, dtype=np.float64) ** 2))
+    f = 4.0 * d * H * s
+    return f / 2 if causal else f
