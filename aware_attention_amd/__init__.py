@@ -1,0 +1,107 @@
+"""MI355X (gfx950) FlashAttention-2 forward: thin Python binding over libfa.so.
+
+Every step of the computation runs in the HIP kernels of libfa.so; this
+module only checks and marshals arguments, allocates outputs through torch
+and passes torch's current HIP stream. There is no fallback path: if the
+library is missing or the device is not a gfx950, calls raise.
+
+    o, lse = fa_fwd(q, k, v, softmax_scale=None, causal=False)
+        q (B,Nq,H,d), k/v (B,Nk,H,d) bfloat16 CUDA tensors -> o (B,Nq,H,d) bf16,
+        lse (B,H,Nq) float32.
+    o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=False)
+        q/k/v (total,H,d), cu_seqlens int32 (num_seqs+1,) on the device ->
+        o (total,H,d), lse (H,total).
+
+The default scale is 1/sqrt(d), as in the definition on "FlashAttention/zh"
+(marovi.ai wiki), section 為何標準注意力運行緩慢. Only half precision on the
+device is accepted and no attention weights are returned, as in
+"InternViT-6B-448px-V1-2 如何加速注意力计算", section
+FlashAttention 封装类三条执行路径 (硬性约束).
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_OK, FaError,
+                   check, load, raw_fa_fwd, raw_fa_fwd_varlen)
+
+__all__ = ["fa_fwd", "fa_fwd_varlen", "FaError", "load", "FA_OK", "FA_ERR_INVALID_ARGUMENT",
+           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_tensor(t, name, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scale(softmax_scale, d):
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None):
+    """Attention forward over an equal-length batch; returns (o, lse)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, 4)
+    B, Nq, H, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    Nk = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, Nq)")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        check(raw_fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, Nq, Nk, H, d, _scale(softmax_scale, d), int(bool(causal)), stream))
+    return out, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=False,
+                  out=None, lse=None):
+    """Attention forward over a packed variable-length batch; returns (o, lse)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, 3)
+    total, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share the packed shape (total, H, d)")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
+            or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
+    num_seqs = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape (H, total)")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        check(raw_fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), cu_seqlens.data_ptr(), num_seqs, int(max_seqlen),
+                                total, H, d, _scale(softmax_scale, d), int(bool(causal)), stream))
+    return out, lse

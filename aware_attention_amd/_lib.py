@@ -1,0 +1,71 @@
+"""ctypes view of libfa.so (the C ABI declared in include/fa.h).
+
+Loading fails loudly: there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_status_string", "fa_last_error", "fa_abi_version")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A libfa call returned a status other than FA_OK."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once (raises OSError naming the path when it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise OSError(f"libfa.so is not built: {LIB_PATH} is missing "
+                      f"(run `python -m aware_attention_amd.build`)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_varlen.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != FA_OK:
+        lib = load()
+        msg = lib.fa_status_string(status).decode()
+        detail = lib.fa_last_error().decode()
+        raise FaError(status, f"libfa: {msg}: {detail}" if detail else f"libfa: {msg}")
+
+
+def raw_fa_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, scale, causal, stream) -> int:
+    """Pointer-level call of fa_fwd; returns the status code."""
+    return load().fa_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, scale, causal, stream)
+
+
+def raw_fa_fwd_varlen(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d, scale,
+                      causal, stream) -> int:
+    """Pointer-level call of fa_fwd_varlen; returns the status code."""
+    return load().fa_fwd_varlen(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d,
+                                scale, causal, stream)

@@ -1,0 +1,191 @@
+// C ABI of libfa.so: argument checks, device check, launch configuration.
+// The operation and the conventions are documented in include/fa.h.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+constexpr int kKeyTile = 64;   // BC: keys per LDS tile
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Per-device answer to "is this a gfx950?", looked up once per device.
+struct DeviceInfo {
+  bool known = false;
+  bool supported = false;
+  std::string arch;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+fa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& info = g_dev[dev];
+  if (!info.known) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(FA_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    info.arch = prop.gcnArchName;
+    info.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    info.known = true;
+  }
+  if (!info.supported) return fail(FA_ERR_UNSUPPORTED, "libfa runs on gfx950 only; device is " + info.arch);
+  return FA_OK;
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_one(const fa::FwdParams& p, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fa::fwd_kernel<D, kKeyTile, CAUSAL, VARLEN>), dim3(grid), dim3(fa::kThreads),
+                     0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t launch(const fa::FwdParams& p, int d, bool causal, uint32_t grid, hipStream_t stream) {
+  switch (d) {
+    case 32: return causal ? launch_one<32, true, VARLEN>(p, grid, stream)
+                           : launch_one<32, false, VARLEN>(p, grid, stream);
+    case 64: return causal ? launch_one<64, true, VARLEN>(p, grid, stream)
+                           : launch_one<64, false, VARLEN>(p, grid, stream);
+    default: return causal ? launch_one<128, true, VARLEN>(p, grid, stream)
+                           : launch_one<128, false, VARLEN>(p, grid, stream);
+  }
+}
+
+fa_status check_common(int32_t H, int32_t d, float scale, int32_t causal) {
+  if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
+  if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
+  return FA_OK;
+}
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                 float softmax_scale, int32_t causal, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (B < 1 || Nq < 1 || Nk < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B, Nq and Nk must be >= 1");
+  fa_status st = check_common(H, d, softmax_scale, causal);
+  if (st != FA_OK) return st;
+  if (causal && Nq != Nk) return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const int64_t n_qt = (Nq + fa::kBR - 1) / fa::kBR;
+  const int64_t grid = n_qt * H * (int64_t)B;
+  if (grid > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.row_stride = (int64_t)H * d;
+  p.q_batch_stride = (int64_t)Nq * H * d;
+  p.k_batch_stride = (int64_t)Nk * H * d;
+  p.lse_head_stride = Nq;
+  p.lse_batch_stride = (int64_t)H * Nq;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.H = H;
+  p.nbatch = B;
+  p.n_qtiles = (int32_t)n_qt;
+  p.scale_log2 = softmax_scale * kLog2e;
+  hipError_t e = launch<false>(p, d, causal != 0, (uint32_t)grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                        int32_t total, int32_t H, int32_t d, float softmax_scale,
+                        int32_t causal, void* stream) {
+  g_last_error.clear();
+  if (!cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
+  if (num_seqs < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
+  if (total < 0 || max_seqlen < 0) return fail(FA_ERR_INVALID_ARGUMENT, "total and max_seqlen must be >= 0");
+  if (max_seqlen > total) return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen exceeds total");
+  fa_status st = check_common(H, d, softmax_scale, causal);
+  if (st != FA_OK) return st;
+  if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned (cu_seqlens 4-byte)");
+  const int64_t n_qt = (max_seqlen + fa::kBR - 1) / fa::kBR;
+  const int64_t grid = n_qt * H * (int64_t)num_seqs;
+  if (grid > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.row_stride = (int64_t)H * d;
+  p.q_batch_stride = 0;
+  p.k_batch_stride = 0;
+  p.lse_head_stride = total;
+  p.lse_batch_stride = 0;
+  p.Nq = 0;
+  p.Nk = 0;
+  p.H = H;
+  p.nbatch = num_seqs;
+  p.n_qtiles = (int32_t)n_qt;
+  p.scale_log2 = softmax_scale * kLog2e;
+  hipError_t e = launch<true>(p, d, causal != 0, (uint32_t)grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+const char* fa_status_string(int32_t status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fa_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+"""Benchmark: attention forward TFLOP/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill8k]
+                    [--no-cpu-baseline]
+
+A step is one fa_fwd call (the whole forward: every query tile, head and
+batch) over the workload's seeded synthetic bf16 inputs, which are resident
+in device memory before timing starts. Timing uses HIP events recorded on the
+stream the kernel runs on (torch's current stream), bracketed by device
+synchronisations. Prints ONE JSON line.
+
+Default workload: B=1, H=32, N=8192, d=128, causal (LLM-prefill shape), the
+configuration the MFMA-utilisation target is quoted on. FLOPs per step are
+4*N*N*d*H*B halved for causal. The CPU baseline is the float64 oracle timed
+on the host on a bounded sample of the same workload (whole heads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention fwd TFLOPS (bf16) and % of MFMA peak, N=1025..8192, d=128"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+KERNEL_SOURCES = [os.path.join(ROOT, "aware_attention_amd", "csrc", f)
+                  for f in ("fa_fwd_kernel.hpp", "fa_api.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("kernel_digest") != kernel_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl: dict, budget_s: float = 12.0):
+    """Time the float64 oracle on whole heads of the workload until budget_s is used."""
+    from oracle import attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = wl["spec"]
+    flops, heads, t0 = 0.0, 0, time.perf_counter()
+    if isinstance(spec, W.Dense):
+        pairs = [(b, h) for b in range(spec.B) for h in range(spec.H)]
+        per_head = spec.flops() / (spec.B * spec.H)
+        for b, h in pairs:
+            f64 = lambda x: W.bf16_bits_to_f32(x[b, :, h]).astype(np.float64)  # noqa: E731
+            attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal)
+            flops += per_head
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        sample = f"{heads} of {len(pairs)} (batch, head) pairs, all {spec.N} rows each"
+    else:
+        cu = wl["cu_seqlens"]
+        for s in range(spec.num_seqs):
+            a, b = int(cu[s]), int(cu[s + 1])
+            for h in range(spec.H):
+                f64 = lambda x: W.bf16_bits_to_f32(x[a:b, h]).astype(np.float64)  # noqa: E731
+                attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal)
+                flops += W.varlen_flops([b - a], 1, spec.d, spec.causal)
+                heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        sample = f"{heads} (sequence, head) pairs of {spec.num_seqs * spec.H}"
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample + f"; float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill8k", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
+              f"forward shards over batch and heads with no exchange, so per-GPU throughput is "
+              f"the one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import aware_attention_amd as aa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wl = W.make_workload(args.workload)
+    spec = wl["spec"]
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    q, k, v = to_dev(wl["q"]), to_dev(wl["k"]), to_dev(wl["v"])
+    o = torch.empty_like(q)
+    if isinstance(spec, W.Dense):
+        lse = torch.empty((spec.B, spec.H, spec.N), dtype=torch.float32, device="cuda")
+        flops = spec.flops()
+        config = {"workload": args.workload, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
+                  "causal": spec.causal}
+
+        def step():
+            aa.fa_fwd(q, k, v, softmax_scale=spec.scale, causal=spec.causal, out=o, lse=lse)
+    else:
+        cu = torch.from_numpy(wl["cu_seqlens"]).cuda()
+        total = q.shape[0]
+        lse = torch.empty((spec.H, total), dtype=torch.float32, device="cuda")
+        flops = W.varlen_flops(wl["lengths"], spec.H, spec.d, spec.causal)
+        config = {"workload": args.workload, "num_seqs": spec.num_seqs, "total": int(total),
+                  "max_seqlen": wl["max_seqlen"], "H": spec.H, "d": spec.d, "causal": spec.causal}
+
+        def step():
+            aa.fa_fwd_varlen(q, k, v, cu, wl["max_seqlen"], softmax_scale=spec.scale,
+                             causal=spec.causal, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    assert torch.isfinite(lse).all(), "non-finite log-sum-exp in the timed output"
+
+    traffic = read_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, shapes of the workload)",
+        "config": config,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_digest": kernel_digest(),
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

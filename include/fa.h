@@ -1,0 +1,107 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) FlashAttention-2 forward library, libfa.so.
+ *
+ * What is computed. For every (batch or sequence, head):
+ *   O = softmax(softmax_scale * Q K^T) V,   L_i = m_i + ln l_i,
+ * with m_i the maximum of row i of the scaled (and masked) scores and
+ * l_i = sum_j exp(S_ij - m_i). The N x N score matrix never reaches memory:
+ * the forward works on query tiles and streams key/value tiles through an
+ * online-softmax update (running max m, running sum l), normalises O by l at
+ * the end and writes the log-sum-exp L per row.
+ *   Definition: "FlashAttention/zh" (marovi.ai wiki), section
+ *     為何標準注意力運行緩慢 (why standard attention is slow).
+ *   Online softmax and the tiled forward with L = m + log l: same page,
+ *     sections 在線 softmax 技巧 and FlashAttention 算法.
+ *   FlashAttention-2 work split (outer loop over query blocks, inner loop over
+ *     key/value blocks): same page, section 變體與後續版本.
+ *   Half-precision only, device tensors only, no attention weights returned,
+ *     packed variable-length batches described by cumulative lengths plus a
+ *     maximum length: "InternViT-6B-448px-V1-2 如何加速注意力计算", section
+ *     FlashAttention 封装类三条执行路径 (硬性约束 and 变长路径).
+ * "log" in L is the natural logarithm.
+ *
+ * Conventions shared by every entry point.
+ *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller, 16-byte aligned, densely packed (row-major, no strides).
+ *     The library keeps no pointer after it returns and allocates no memory.
+ *   - Q, K, V and O are bfloat16 (passed as void*); L is float32.
+ *   - Head dimension d must be 32, 64 or 128.
+ *   - softmax_scale must be finite and >= 0 (callers normally pass 1/sqrt(d)).
+ *   - causal = 1 applies the lower-triangular mask of self-attention (query i
+ *     sees keys j <= i) and needs as many queries as keys; causal = 0 is
+ *     unmasked attention.
+ *   - stream is a hipStream_t (NULL = the null stream). The call only enqueues
+ *     work: it returns before the GPU has finished, and a fault inside the
+ *     kernel surfaces at the caller's next synchronisation.
+ *   - Errors: arguments are checked on the host before any HIP call; a bad
+ *     argument returns FA_ERR_INVALID_ARGUMENT, an unsupported shape or device
+ *     FA_ERR_UNSUPPORTED, a failed HIP call FA_ERR_HIP. Nothing is enqueued
+ *     when a check fails. fa_last_error() gives a message for the calling
+ *     thread's most recent failure.
+ *   - Thread-safe. Outputs may not alias inputs.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_HIP = 3
+} fa_status;
+
+/*
+ * Equal-length batch.
+ *   q   : (B, Nq, H, d) bfloat16
+ *   k, v: (B, Nk, H, d) bfloat16
+ *   o   : (B, Nq, H, d) bfloat16, written
+ *   lse : (B, H, Nq)    float32,  written (natural-log log-sum-exp per row)
+ * Requires B, Nq, Nk, H >= 1; causal requires Nq == Nk. Every element of o
+ * and lse is written; nothing else is touched.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                 float softmax_scale, int32_t causal, void* stream);
+
+/*
+ * Packed variable-length batch (no padding).
+ *   q, k, v, o : (total, H, d) bfloat16; o written
+ *   lse        : (H, total) float32, written
+ *   cu_seqlens : DEVICE int32[num_seqs + 1]; sequence s occupies rows
+ *                [cu_seqlens[s], cu_seqlens[s+1]) of q, k, v and o and attends
+ *                only to its own rows. The contents must satisfy
+ *                cu_seqlens[0] = 0, non-decreasing, cu_seqlens[num_seqs] = total
+ *                and every length <= max_seqlen; they live on the device and
+ *                are not checked by the library (rows outside every sequence
+ *                are not written; lengths above max_seqlen are not processed
+ *                past max_seqlen).
+ * Requires num_seqs >= 1, H >= 1, total >= 0, max_seqlen >= 0 (0 or total = 0
+ * enqueues nothing). Queries and keys share the boundaries, so causal masking
+ * is per sequence.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                        int32_t total, int32_t H, int32_t d, float softmax_scale,
+                        int32_t causal, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* fa_status_string(int32_t status);
+
+/* Message for the calling thread's most recent failed call ("" if none).
+ * The pointer stays valid until the thread's next call into the library. */
+const char* fa_last_error(void);
+
+/* Version of this ABI (incremented on incompatible change). */
+int32_t fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

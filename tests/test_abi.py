@@ -1,0 +1,140 @@
+"""The C ABI on the host: exports, status strings, argument checks (no GPU needed).
+
+Every check here is taken on the host before any HIP call, so a bad argument
+returns an error code and enqueues nothing. Pointer values used below are
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+aa = pytest.importorskip("aware_attention_amd")
+from aware_attention_amd import _lib  # noqa: E402
+
+INV, UNS, HIP = _lib.FA_ERR_INVALID_ARGUMENT, _lib.FA_ERR_UNSUPPORTED, _lib.FA_ERR_HIP
+P = 0x10000          # a 16-byte aligned stand-in pointer; never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    return _lib.load()
+
+
+def test_header_declares_the_abi():
+    assert _declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib_or_skip()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.fa_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib_or_skip()
+    for s in range(4):
+        assert lib.fa_status_string(s)
+    assert lib.fa_status_string(99) == b"unknown status"
+    assert lib.fa_last_error() is not None
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Nq=128, Nk=128, H=2, d=64, scale=0.125,
+             causal=0, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Nq"], a["Nk"],
+                           a["H"], a["d"], a["scale"], a["causal"], a["stream"])
+
+
+def _varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cu=P, num_seqs=2, max_seqlen=100, total=150, H=2, d=128,
+             scale=0.1, causal=0, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["num_seqs"],
+                                  a["max_seqlen"], a["total"], a["H"], a["d"], a["scale"],
+                                  a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(o=None), INV),
+    (dict(lse=None), INV),
+    (dict(B=0), INV), (dict(Nq=0), INV), (dict(Nk=-1), INV), (dict(H=0), INV),
+    (dict(causal=2), INV), (dict(causal=1, Nq=128, Nk=64), INV),
+    (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
+    (dict(q=P + 8), INV), (dict(o=P + 2), INV), (dict(lse=P + 4), INV),
+    (dict(d=48), UNS), (dict(d=256), UNS), (dict(scale=-0.5), UNS),
+])
+def test_fa_fwd_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _fwd(**kw) == code
+    assert _lib.load().fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), INV), (dict(num_seqs=0), INV), (dict(total=-1), INV),
+    (dict(max_seqlen=-1), INV), (dict(max_seqlen=200, total=150), INV),
+    (dict(q=None), INV), (dict(v=P + 4), INV), (dict(cu=P + 2), INV),
+    (dict(causal=3), INV), (dict(scale=float("nan")), INV), (dict(d=80), UNS),
+])
+def test_fa_fwd_varlen_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _varlen(**kw) == code
+
+
+def test_varlen_empty_batch_enqueues_nothing():
+    _lib_or_skip()
+    assert _varlen(total=0, max_seqlen=0, q=None, k=None, v=None, o=None, lse=None) == _lib.FA_OK
+    assert _varlen(max_seqlen=0) == _lib.FA_OK
+
+
+def test_valid_call_without_a_device_is_a_hip_error():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _fwd() == HIP
+    assert b"hip" in _lib.load().fa_last_error().lower()
+
+
+def test_binding_rejects_host_tensors_and_wrong_dtype():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        aa.fa_fwd(x, x, x)
+    with pytest.raises(TypeError):
+        aa.fa_fwd(x.float(), x, x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libfa.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(OSError, match="libfa.so"):
+        _lib.load()
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package and the oracle share no code and import nothing from each other."""
+    pkg = os.path.join(ROOT, "aware_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", src, re.M), f
+                assert "oracle/" not in src, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            src = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
+            assert "aware_attention_amd" not in src and "workloads" not in src, f
