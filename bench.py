@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill8k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device-to-device copy of 1 GiB (3 times), to "
+                         "calibrate HBM byte counters against a known size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,6 +127,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src_t = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                          "launches": 3}), flush=True)
+        return
     wl = W.make_workload(args.workload)
     spec = wl["spec"]
     to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
