@@ -8,12 +8,24 @@
 //     each of its 4 wavefronts owns 32 of those rows and keeps its Q rows in
 //     VGPRs for the whole kernel;
 //   * streams key/value tiles of BC keys through LDS, double-buffered: the
-//     next tile's global loads are in flight while the current one is used;
+//     global loads of later tiles are in flight while the current ones are used;
 //   * per tile, per wavefront: S^T = K Q^T on bf16 MFMA (fp32 accumulate),
 //     online-softmax update in base 2 (running max m, running sum l, rescale
 //     of the output accumulator by exp2(m_old - m_new)), then
 //     O^T += V^T P^T on bf16 MFMA with P rounded to bf16;
 //   * finally O = O_acc / l goes out as bf16 and L = ln2 * (m + log2 l) as fp32.
+//
+// Software pipeline. Keys run one tile ahead of values: while the VALU does
+// the softmax of tile j, the matrix cores already compute S^T of tile j+1, so
+// the exponentials overlap MFMA work inside one wavefront. K and V have their
+// own pair of LDS buffers; one barrier per tile orders the buffer reuse.
+//
+// Deferred rescaling. The running maximum m used as the exponent offset is
+// moved only when some row's tile maximum exceeds it by more than kRescaleTau
+// (base-2 units); otherwise the tile is exponentiated against the stale m, so
+// P~ can reach 2^kRescaleTau. In exact arithmetic the result is unchanged:
+// O = sum P~ V / sum P~ and L = m + log l are invariant to the offset. This
+// removes the per-tile multiply of the whole output accumulator.
 //
 // Layout choices (gfx950 v_mfma_f32_32x32x16_bf16, wave64):
 //   MFMA A operand: lane l holds A[m = l%32][k = 8*(l/32) .. +7];
@@ -43,6 +55,7 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -72,37 +85,55 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kRescaleTau = 8.0f;
 
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
-}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // Key order inside LDS rows of V^T: swap bits 2 and 3 of the key index.
 __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// LDS tile layout shared by K and V: BC rows of D bf16 (2*D bytes), no
+// padding, 16-byte chunks permuted inside each row by an XOR with a
+// row-dependent mask so that the MFMA operand reads hit distinct LDS banks.
+template <int D>
+struct TileLayout {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;          // 16-byte chunks per row
+  // K operand reads: 16 consecutive rows, one chunk each -> 16 distinct banks.
+  __device__ static constexpr int k_swz(int row) {
+    return D == 128 ? (row & 15) : D == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  }
+  // V operand reads (transposing 8-byte reads): 4 consecutive rows x 8 chunks
+  // of 8 bytes per half-wave -> 32 distinct bank pairs.
+  __device__ static constexpr int v_swz(int row) {
+    return D == 128 ? 4 * (row & 3) : D == 64 ? 4 * ((row >> 1) & 1) : 0;
+  }
+};
+
 template <int D, int BC, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
-  static_assert(BC % 32 == 0 && BC >= 32 && BC <= 128, "key tile");
-  constexpr int KS = D + 8;            // LDS row stride of K (elements)
-  constexpr int VS = BC + 8;           // LDS row stride of V^T (elements)
-  constexpr int K_ELEMS = BC * KS;
-  constexpr int V_ELEMS = D * VS;
-  constexpr int BUF = K_ELEMS + V_ELEMS;
-  constexpr int KB = BC / 32;          // 32-key blocks per tile
-  constexpr int DS = D / 16;           // MFMA k-steps over d
-  constexpr int DB = D / 32;           // 32-wide d blocks of O^T
-  constexpr int KCH = BC * D / 8;      // 16-byte chunks in a K tile
-  static_assert(KCH % kThreads == 0, "K tile split");
-  constexpr int K_PER_T = KCH / kThreads;
-  constexpr int NVB = (BC / 4) * (D / 8);   // 4-key x 8-d blocks in a V tile
-  static_assert(NVB <= kThreads, "V tile split");
+  static_assert(BC == 64, "key tile");
+  using TL = TileLayout<D>;
+  constexpr int RB = TL::kRowBytes;
+  constexpr int TILE_BYTES = BC * RB;            // one K or V tile
+  constexpr int KB = BC / 32;                    // 32-key blocks per tile
+  constexpr int DS = D / 16;                     // MFMA k-steps over d
+  constexpr int DB = D / 32;                     // 32-wide d blocks of O^T
+  constexpr int NPW = TILE_BYTES / 1024 / kWaves;  // 1 KiB direct loads per wave per tile
+  static_assert(NPW >= 1 && TILE_BYTES % (1024 * kWaves) == 0, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+  // [K buf 0][K buf 1][V buf 0][V buf 1]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,9 +170,10 @@ void fwd_kernel(FwdParams p) {
   if (q0 >= Nq) return;   // whole workgroup: tile past this sequence's end
 
   const uint16_t* __restrict__ qg = p.q + q_off;
-  const uint16_t* __restrict__ kg = p.k + k_off;
-  const uint16_t* __restrict__ vg = p.v + k_off;
-  const int64_t rs = p.row_stride;
+  const uint8_t* __restrict__ kg = reinterpret_cast<const uint8_t*>(p.k + k_off);
+  const uint8_t* __restrict__ vg = reinterpret_cast<const uint8_t*>(p.v + k_off);
+  const int rs = (int)p.row_stride;          // elements
+  const int rs_bytes = 2 * rs;
   const float s2 = p.scale_log2;
 
   const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
@@ -151,6 +183,8 @@ void fwd_kernel(FwdParams p) {
   const int qw0 = q0 + wave * 32;        // first query row of this wavefront
   const int qrow = qw0 + l32;            // this lane's query row
   const bool wave_has_rows = qw0 < Nq;
+  // Last key tile that has a visible key for some row of this wavefront.
+  const int wave_last_kt = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BC) : n_kt - 1;
   bf16x8 qr[DS];
   if (qrow < Nq) {
     const u32x4* src = reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * rs);
@@ -161,54 +195,81 @@ void fwd_kernel(FwdParams p) {
     for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
-  // ---- staging registers for the next K/V tile ----
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[4];
-  const int vkq = tid % (BC / 4);        // this thread's 4-key group of V
-  const int vdc = tid / (BC / 4);        // this thread's 8-wide d chunk of V
-
-  auto load_tile = [&](int kt) {
+  // ---- direct HBM -> LDS copies: this lane's slot in each of the wave's loads ----
+  // Slot s of a tile (16 bytes at byte 16*s) holds row s / kChunks, logical
+  // chunk (s % kChunks) ^ swz(row).
+  int cp_row[NPW], k_src[NPW], v_src[NPW];
+#pragma unroll
+  for (int n = 0; n < NPW; ++n) {
+    const int slot = (wave * NPW + n) * 64 + lane;
+    const int row = slot / TL::kChunks;
+    const int phys = slot % TL::kChunks;
+    cp_row[n] = row;
+    k_src[n] = row * rs_bytes + ((phys ^ TL::k_swz(row)) * 16);
+    v_src[n] = row * rs_bytes + ((phys ^ TL::v_swz(row)) * 16);
+  }
+  auto copy_tile = [&](const uint8_t* gsrc, const int (&src)[NPW], int tile_base, int kt) {
     const int k0 = kt * BC;
+    const uint8_t* g = gsrc + (int64_t)k0 * rs_bytes;
+    if (k0 + BC <= Nk) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8);
-      const int col = c % (D / 8);
-      const int key = k0 + row;
-      kreg[i] = key < Nk ? *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + col * 8)
-                         : u32x4{0, 0, 0, 0};
-    }
-    if (tid < NVB) {
+      for (int n = 0; n < NPW; ++n)
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(g + src[n]),
+            (__attribute__((address_space(3))) void*)(smem + tile_base + (wave * NPW + n) * 1024),
+            16, 0, 0);
+    } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * vkq + r;
-        vreg[r] = key < Nk ? *reinterpret_cast<const u32x4*>(vg + (int64_t)key * rs + vdc * 8)
-                           : u32x4{0, 0, 0, 0};
+      for (int n = 0; n < NPW; ++n) {
+        if (k0 + cp_row[n] < Nk) {
+          __builtin_amdgcn_global_load_lds(
+              (__attribute__((address_space(1))) void*)(g + src[n]),
+              (__attribute__((address_space(3))) void*)(smem + tile_base + (wave * NPW + n) * 1024),
+              16, 0, 0);
+        } else {
+          *reinterpret_cast<u32x4*>(smem + tile_base + (wave * NPW + n) * 1024 + 16 * lane) =
+              u32x4{0, 0, 0, 0};
+        }
       }
     }
   };
+  auto copy_k = [&](int kt, int buf) { copy_tile(kg, k_src, buf * TILE_BYTES, kt); };
+  auto copy_v = [&](int kt, int buf) { copy_tile(vg, v_src, (2 + buf) * TILE_BYTES, kt); };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * BUF;
-    uint16_t* Vt = Ks + K_ELEMS;
+  // ---- LDS operand addresses of this lane ----
+  // K operand (A of S^T = K Q^T): row 32*kb + l32, logical chunk 2*ds + hi.
+  int k_rd[DS];
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8);
-      const int col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(Ks + row * KS + col * 8) = kreg[i];
-    }
-    if (tid < NVB) {
-      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys (8 bytes) each.
-      const int pos = vt_pos(4 * vkq);
+  for (int ds = 0; ds < DS; ++ds) k_rd[ds] = l32 * RB + (((2 * ds + hi) ^ TL::k_swz(l32)) * 16);
+  // V operand (A of O^T = V^T P^T) by transposing 8-byte reads: in each group
+  // of 16 lanes, lane i reads row base + 4*hi + i/4, dims 32*b + 16*half + 4*(i%4);
+  // the transpose hands lane j dims 32*b + 16*half + j of four consecutive rows.
+  const int vg16 = lane >> 4, vi = lane & 15;
+  const int v_row = 4 * hi + (vi >> 2);
+  const int v_x = 2 * (vg16 & 1) + ((vi & 3) >> 1);
+  int v_rd[DB];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo_e = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        const uint32_t hi_e = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-        const uint32_t lo_o = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        const uint32_t hi_o = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        *reinterpret_cast<u32x2*>(Vt + (vdc * 8 + 2 * w) * VS + pos) = u32x2{lo_e, hi_e};
-        *reinterpret_cast<u32x2*>(Vt + (vdc * 8 + 2 * w + 1) * VS + pos) = u32x2{lo_o, hi_o};
+  for (int b = 0; b < DB; ++b)
+    v_rd[b] = v_row * RB + (((4 * b + v_x) ^ TL::v_swz(v_row)) * 16) + 8 * (vi & 1);
+
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  auto lds_b128 = [&](int byte) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(smem + byte);
+  };
+  auto lds_tr = [&](int byte) -> v4i16 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint8_t*)smem + byte));
+  };
+
+  // S^T of one tile for this wavefront: BC keys x 32 queries, fp32.
+  auto qk = [&](f32x16 (&s)[KB], int kbuf) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 a = lds_b128(kbuf * TILE_BYTES + 32 * kb * RB + k_rd[ds]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
       }
     }
   };
@@ -217,94 +278,137 @@ void fwd_kernel(FwdParams p) {
   f32x16 o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b] = f32x16{};
-  float m_run = kNegInf;   // running max, base-2 units of the scaled score
+  float m_run = kNegInf;   // exponent offset, base-2 units of the scaled score
   float l_run = 0.f;       // running sum over this lane's half of the keys
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Softmax pieces. need_mask: the tile holds keys past the end or, when
+  // causal, keys after some query of this wavefront.
+  auto need_mask = [&](int k0) { return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0); };
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const bool more = kt + 1 < n_kt;
-    if (more) load_tile(kt + 1);
-    const int k0 = kt * BC;
-    const bool active = wave_has_rows && (!CAUSAL || k0 <= qw0 + 31);
-    if (active) {
-      const uint16_t* Ks = smem + (kt & 1) * BUF;
-      const uint16_t* Vt = Ks + K_ELEMS;
-
-      // S^T = K Q^T for BC keys x 32 queries.
-      f32x16 s[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* krow = Ks + (32 * kb + l32) * KS + 8 * hi;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ds);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
-        }
-      }
-
-      // Online softmax, base 2.
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0);
-      float mt = kNegInf;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool ok = key < Nk && (!CAUSAL || key <= qrow);
-            const float t = s[kb][r] * s2;
-            s[kb][r] = ok ? t : kNegInf;
-            mt = fmaxf(mt, s[kb][r]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-        }
-        mt *= s2;
-      }
-      mt = fmaxf(mt, xor32(mt));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float rsum = 0.f;
-      bf16x8 pb[KB][2];
+  // Row maximum of the tile in base-2 units, shared by the two lanes of a row.
+  // The masked form scales and masks s in place.
+  auto rowmax = [&](f32x16 (&s)[KB], bool masked, int k0) {
+    float mt = kNegInf;
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = need_mask ? s[kb][r] - m_new : __builtin_fmaf(s[kb][r], s2, -m_new);
-          const float e = __builtin_amdgcn_exp2f(x);
-          rsum += e;
-          pb[kb][r >> 3][r & 7] = (__bf16)e;
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = key < Nk && (!CAUSAL || key <= qrow);
+          s[kb][r] = ok ? s[kb][r] * s2 : kNegInf;
+          mt = fmaxf(mt, s[kb][r]);
         }
       }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
+      }
+      mt *= s2;
+    }
+    return fmaxf(mt, xor32(mt));
+  };
+
+  // Move the exponent offset only when some row grew by more than kRescaleTau.
+  auto maybe_rescale = [&](float mt) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      m_run = m_new;
+    }
+  };
 
-      // O^T += V^T P^T.
+  // P~ = exp2(scaled score - m) rounded to bf16 pairs; fp32 row sums of P~.
+  auto exp_pack = [&](const f32x16 (&s)[KB], bf16x8 (&pb)[KB][2], bool prescaled) {
+    const float neg_m = -m_run;
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const uint16_t* vrow = Vt + (32 * b + l32) * VS + 8 * hi;
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 32 * kb + 16 * t);
-            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], o[b], 0, 0, 0);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * t + 2 * i;
+          const float x0 = prescaled ? s[kb][r] + neg_m : __builtin_fmaf(s[kb][r], s2, neg_m);
+          const float x1 = prescaled ? s[kb][r + 1] + neg_m : __builtin_fmaf(s[kb][r + 1], s2, neg_m);
+          const float e0 = __builtin_amdgcn_exp2f(x0);
+          const float e1 = __builtin_amdgcn_exp2f(x1);
+          w[i] = pack_bf16(e0, e1);
+          l_run += e0 + e1;
+        }
+        pb[kb][t] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  };
+
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](const bf16x8 (&pb)[KB][2], int vbuf) {
+    const int base = (2 + vbuf) * TILE_BYTES;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r0 = (32 * kb + 16 * t) * RB;
+          const v4i16 lo = lds_tr(base + r0 + v_rd[b]);
+          const v4i16 up = lds_tr(base + r0 + 8 * RB + v_rd[b]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], o[b], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile((kt + 1) & 1);
+  };
+
+  // All of this thread's direct LDS copies have landed and every thread's are
+  // visible: wait for the memory counters, then the workgroup barrier.
+  auto tile_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  // ---- prologue: K_0 -> Kbuf0, V_0 -> Vbuf0, K_1 -> Kbuf1, S_0 ----
+  copy_k(0, 0);
+  copy_v(0, 0);
+  if (n_kt > 1) copy_k(1, 1);
+  tile_sync();
+  f32x16 s_cur[KB];
+  if (wave_has_rows) qk(s_cur, 0);
+  __syncthreads();   // every wave is done with Kbuf0 before it is refilled
+
+  // ---- main loop: tile j's softmax and P V, tile j+1's S ----
+  for (int j = 0; j < n_kt; ++j) {
+    if (j + 2 < n_kt) copy_k(j + 2, j & 1);
+    if (j + 1 < n_kt) copy_v(j + 1, (j + 1) & 1);
+    const bool act_j = wave_has_rows && j <= wave_last_kt;
+    const bool act_j1 = wave_has_rows && j + 1 <= wave_last_kt;
+    f32x16 s_next[KB];
+    bf16x8 pb[KB][2];
+    const int k0 = j * BC;
+    const bool masked = need_mask(k0);
+    if (act_j && act_j1 && !masked) {
+      // Common case, one basic block: tile j+1's QK^T on the matrix cores
+      // alongside tile j's exponentials, then tile j's P V.
+      maybe_rescale(rowmax(s_cur, false, k0));
+      qk(s_next, (j + 1) & 1);
+      exp_pack(s_cur, pb, false);
+      pv(pb, j & 1);
+    } else {
+      if (act_j1) qk(s_next, (j + 1) & 1);
+      if (act_j) {
+        maybe_rescale(rowmax(s_cur, masked, k0));
+        exp_pack(s_cur, pb, masked);
+        pv(pb, j & 1);
+      }
+    }
+    tile_sync();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_next[kb];
   }
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
@@ -318,7 +422,7 @@ void fwd_kernel(FwdParams p) {
       for (int g = 0; g < 4; ++g) {
         bf16x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[b][4 * g + j] * inv);
+        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(o[b][4 * g + jj] * inv);
         *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * hi) = w;
       }
     }
