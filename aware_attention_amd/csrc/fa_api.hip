@@ -14,8 +14,6 @@
 
 namespace {
 
-constexpr int kKeyTile = 64;   // BC: keys per LDS tile
-
 thread_local std::string g_last_error;
 
 fa_status fail(fa_status s, const std::string& msg) {
@@ -57,7 +55,7 @@ fa_status check_device() {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const fa::FwdParams& p, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa::fwd_kernel<D, kKeyTile, CAUSAL, VARLEN>), dim3(grid), dim3(fa::kThreads),
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(fa::kThreads),
                      0, stream, p);
   return hipGetLastError();
 }

@@ -4,21 +4,26 @@
 // FlashAttention 算法, with the FlashAttention-2 loop order of section
 // 變體與後續版本: outer loop over query blocks spread across the grid, inner
 // loop over key/value blocks inside the workgroup):
-//   * owns one query tile of BR = 128 rows of one (batch or sequence, head);
-//     each of its 4 wavefronts owns 32 of those rows and keeps its Q rows in
+//   * owns one query tile of BR = 256 rows of one (batch or sequence, head);
+//     each of its 8 wavefronts owns 32 of those rows and keeps its Q rows in
 //     VGPRs for the whole kernel;
-//   * streams key/value tiles of BC keys through LDS, double-buffered: the
-//     global loads of later tiles are in flight while the current ones are used;
+//   * streams key/value tiles of BC = 64 keys through LDS, double-buffered,
+//     copied straight from HBM into LDS (global_load_lds_dwordx4);
 //   * per tile, per wavefront: S^T = K Q^T on bf16 MFMA (fp32 accumulate),
 //     online-softmax update in base 2 (running max m, running sum l, rescale
 //     of the output accumulator by exp2(m_old - m_new)), then
 //     O^T += V^T P^T on bf16 MFMA with P rounded to bf16;
 //   * finally O = O_acc / l goes out as bf16 and L = ln2 * (m + log2 l) as fp32.
 //
-// Software pipeline. Keys run one tile ahead of values: while the VALU does
-// the softmax of tile j, the matrix cores already compute S^T of tile j+1, so
-// the exponentials overlap MFMA work inside one wavefront. K and V have their
-// own pair of LDS buffers; one barrier per tile orders the buffer reuse.
+// Two wave groups in ping-pong. Waves 0-3 (group A, rows 0-127) and waves 4-7
+// (group B, rows 128-255) share the four SIMDs of a CU, one wave of each
+// group per SIMD. Every tile is split into two phases that end at a
+// workgroup barrier:
+//   M phase (matrix cores): S^T of tile j, and O^T += V^T P^T of tile j-1;
+//   V phase (vector ALU):   the online softmax of tile j, giving P of tile j.
+// Group B runs one phase behind group A, so on every SIMD one wave issues
+// MFMAs while the other does exponentials: the softmax hides under the matrix
+// work without software pipelining inside a wave.
 //
 // Deferred rescaling. The running maximum m used as the exponent offset is
 // moved only when some row's tile maximum exceeds it by more than kRescaleTau
@@ -37,9 +42,9 @@
 // lane l and lane l^32. The accumulator registers of S^T feed the B operand
 // of the P V product directly, with no trip through LDS: register group
 // r = 8t..8t+7 of a 32-key block holds keys 16t + {0..3, 8..11} + 4*(l/32).
-// V is written to LDS transposed, with the key order inside every group of 16
-// keys permuted (bits 2 and 3 of the key index swapped), so the eight keys a
-// lane needs for one MFMA are contiguous: one 16-byte LDS read per operand.
+// K and V sit in LDS row-major; the V^T operand comes from transposing 8-byte
+// reads (ds_read_b64_tr_b16), addressed so the transpose hands each lane the
+// keys in exactly that order.
 //
 // Masking ("FlashAttention/zh", section 變體與後續版本: causal masks):
 // keys past the sequence end and, when causal, keys after the query are set
@@ -51,6 +56,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -58,7 +65,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 struct FwdParams {
   const uint16_t* q;
@@ -80,23 +87,52 @@ struct FwdParams {
   float scale_log2;            // softmax_scale * log2(e), >= 0
 };
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                 // two groups of four
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBR = 32 * kWaves;
+constexpr int kBR = 32 * kWaves;          // query rows per workgroup
+constexpr int kBC = 64;                   // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kRescaleTau = 8.0f;
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-// Key order inside LDS rows of V^T: swap bits 2 and 3 of the key index.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// max(a, b, c) in one v_max3_f32. Written as inline asm: the generic fmaxf
+// route quiets each MFMA result with an extra v_max before comparing, which
+// doubles the cost of the row maximum. NaN scores still reach the output:
+// they are dropped from the maximum but not from exp2(score - m).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Workgroup barrier without a memory fence: LDS operand reads of the current
+// tiles may stay in flight across it (they are read-only). The copies into
+// LDS are made visible explicitly (s_waitcnt by the issuing waves before the
+// barrier that publishes them).
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l's
+// 16 bytes from gptr land at LDS byte lds_base + 16*l (lds_base must be the
+// same in every lane of the wave). Issued as inline asm
+// on purpose: the compiler would otherwise treat every later LDS read as a
+// possible reader of this asynchronous write and wait for the copy to land
+// before it, even when (as here, by construction) the reads target another
+// buffer. The instruction has no register outputs; the kernel itself waits
+// for the copies (s_waitcnt vmcnt) before the barrier that publishes them.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
 }
 
 // LDS tile layout shared by K and V: BC rows of D bf16 (2*D bytes), no
@@ -117,29 +153,35 @@ struct TileLayout {
   }
 };
 
-template <int D, int BC, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
-  static_assert(BC == 64, "key tile");
+  constexpr int BC = kBC;
   using TL = TileLayout<D>;
   constexpr int RB = TL::kRowBytes;
   constexpr int TILE_BYTES = BC * RB;            // one K or V tile
   constexpr int KB = BC / 32;                    // 32-key blocks per tile
   constexpr int DS = D / 16;                     // MFMA k-steps over d
   constexpr int DB = D / 32;                     // 32-wide d blocks of O^T
-  constexpr int NPW = TILE_BYTES / 1024 / kWaves;  // 1 KiB direct loads per wave per tile
-  static_assert(NPW >= 1 && TILE_BYTES % (1024 * kWaves) == 0, "tile split");
+  constexpr int NCP = TILE_BYTES / 1024;         // 1 KiB direct copies per tile
+  constexpr int NPW = NCP / 4;                   // ... per wave of group A
+  static_assert(NCP % 4 == 0 && NPW >= 1, "tile split");
 
   // [K buf 0][K buf 1][V buf 0][V buf 1]
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
+
+  // LDS byte address of smem (the low 32 bits of its flat address).
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const bool group_b = wave >= 4;
+  const int gw = wave & 3;               // wave index inside its group
 
   // ---- work item: (query tile, head, batch or sequence) ----
   const int per_qt = p.H * p.nbatch;
@@ -195,13 +237,13 @@ void fwd_kernel(FwdParams p) {
     for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
-  // ---- direct HBM -> LDS copies: this lane's slot in each of the wave's loads ----
+  // ---- direct HBM -> LDS copies, issued by the waves of group A ----
   // Slot s of a tile (16 bytes at byte 16*s) holds row s / kChunks, logical
   // chunk (s % kChunks) ^ swz(row).
   int cp_row[NPW], k_src[NPW], v_src[NPW];
 #pragma unroll
   for (int n = 0; n < NPW; ++n) {
-    const int slot = (wave * NPW + n) * 64 + lane;
+    const int slot = (gw * NPW + n) * 64 + lane;
     const int row = slot / TL::kChunks;
     const int phys = slot % TL::kChunks;
     cp_row[n] = row;
@@ -211,30 +253,24 @@ void fwd_kernel(FwdParams p) {
   auto copy_tile = [&](const uint8_t* gsrc, const int (&src)[NPW], int tile_base, int kt) {
     const int k0 = kt * BC;
     const uint8_t* g = gsrc + (int64_t)k0 * rs_bytes;
+    const uint32_t lds0 = smem_lds + tile_base + gw * NPW * 1024;
     if (k0 + BC <= Nk) {
 #pragma unroll
-      for (int n = 0; n < NPW; ++n)
-        __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void*)(g + src[n]),
-            (__attribute__((address_space(3))) void*)(smem + tile_base + (wave * NPW + n) * 1024),
-            16, 0, 0);
+      for (int n = 0; n < NPW; ++n) copy16_to_lds(g + src[n], lds0 + n * 1024);
     } else {
 #pragma unroll
       for (int n = 0; n < NPW; ++n) {
         if (k0 + cp_row[n] < Nk) {
-          __builtin_amdgcn_global_load_lds(
-              (__attribute__((address_space(1))) void*)(g + src[n]),
-              (__attribute__((address_space(3))) void*)(smem + tile_base + (wave * NPW + n) * 1024),
-              16, 0, 0);
+          copy16_to_lds(g + src[n], lds0 + n * 1024);
         } else {
-          *reinterpret_cast<u32x4*>(smem + tile_base + (wave * NPW + n) * 1024 + 16 * lane) =
+          *reinterpret_cast<u32x4*>(smem + tile_base + (gw * NPW + n) * 1024 + 16 * lane) =
               u32x4{0, 0, 0, 0};
         }
       }
     }
   };
-  auto copy_k = [&](int kt, int buf) { copy_tile(kg, k_src, buf * TILE_BYTES, kt); };
-  auto copy_v = [&](int kt, int buf) { copy_tile(vg, v_src, (2 + buf) * TILE_BYTES, kt); };
+  auto copy_k = [&](int kt) { copy_tile(kg, k_src, (kt & 1) * TILE_BYTES, kt); };
+  auto copy_v = [&](int kt) { copy_tile(vg, v_src, (2 + (kt & 1)) * TILE_BYTES, kt); };
 
   // ---- LDS operand addresses of this lane ----
   // K operand (A of S^T = K Q^T): row 32*kb + l32, logical chunk 2*ds + hi.
@@ -252,7 +288,6 @@ void fwd_kernel(FwdParams p) {
   for (int b = 0; b < DB; ++b)
     v_rd[b] = v_row * RB + (((4 * b + v_x) ^ TL::v_swz(v_row)) * 16) + 8 * (vi & 1);
 
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
   auto lds_b128 = [&](int byte) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(smem + byte);
   };
@@ -261,35 +296,80 @@ void fwd_kernel(FwdParams p) {
         (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint8_t*)smem + byte));
   };
 
-  // S^T of one tile for this wavefront: BC keys x 32 queries, fp32.
-  auto qk = [&](f32x16 (&s)[KB], int kbuf) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 a = lds_b128(kbuf * TILE_BYTES + 32 * kb * RB + k_rd[ds]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
-      }
-    }
-  };
-
   // ---- running state (one query row per lane) ----
   f32x16 o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b] = f32x16{};
   float m_run = kNegInf;   // exponent offset, base-2 units of the scaled score
   float l_run = 0.f;       // running sum over this lane's half of the keys
+  f32x16 s[KB];            // S^T of the current tile
+  bf16x8 pb[KB][2];        // P~ of the previous tile, as MFMA B operands
 
-  // Softmax pieces. need_mask: the tile holds keys past the end or, when
-  // causal, keys after some query of this wavefront.
-  auto need_mask = [&](int k0) { return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0); };
+  // S^T = K Q^T for one tile (BC keys x 32 queries).
+  auto qk = [&](int kt) {
+    const int base = (kt & 1) * TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {   // alternate accumulators
+        const bf16x8 a = lds_b128(base + 32 * kb * RB + k_rd[ds]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
+      }
+    }
+  };
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](int kt) {
+    const int base = (2 + (kt & 1)) * TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {   // alternate accumulators
+          const int r0 = (32 * kb + 16 * t) * RB;
+          const v4i16 lo = lds_tr(base + r0 + v_rd[b]);
+          const v4i16 up = lds_tr(base + r0 + 8 * RB + v_rd[b]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], o[b], 0, 0, 0);
+        }
+      }
+    }
+  };
 
-  // Row maximum of the tile in base-2 units, shared by the two lanes of a row.
-  // The masked form scales and masks s in place.
-  auto rowmax = [&](f32x16 (&s)[KB], bool masked, int k0) {
+  // M phase with both products: the QK^T MFMAs of tile kt and the P V MFMAs
+  // of tile kt-1 alternate, and each product walks its accumulators in turn
+  // (S^T: 2 blocks, O^T: DB blocks), so consecutive MFMAs never depend on
+  // each other and the matrix pipe never waits for its own previous result.
+  auto qk_pv = [&](int kt) {
+    constexpr int N = KB * DS;                   // == DB * KB * 2
+    static_assert(N == DB * KB * 2, "interleave");
+    const int kbase = (kt & 1) * TILE_BYTES;
+    const int vbase = (2 + ((kt - 1) & 1)) * TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ds = i / KB, kb = i % KB;
+      const bf16x8 a = lds_b128(kbase + 32 * kb * RB + k_rd[ds]);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
+      const int b = i % DB, c = i / DB, kb2 = c / 2, t = c % 2;
+      const int r0 = (32 * kb2 + 16 * t) * RB;
+      const v4i16 lo = lds_tr(vbase + r0 + v_rd[b]);
+      const v4i16 up = lds_tr(vbase + r0 + 8 * RB + v_rd[b]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb2][t], o[b], 0, 0, 0);
+    }
+  };
+
+  // Online softmax of one tile: s -> pb, updating m_run, l_run and (rarely) o.
+  // Instantiated separately for tiles that need the mask and tiles that do
+  // not, so the common path carries no per-element selects.
+  auto softmax_tile = [&](auto masked_tag, int k0) {
+    constexpr bool masked = decltype(masked_tag)::value;
     float mt = kNegInf;
-    if (masked) {
+    if constexpr (masked) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -304,16 +384,15 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
+        for (int r = 0; r < 16; r += 2) mt = max3(mt, s[kb][r], s[kb][r + 1]);
       }
       mt *= s2;
     }
-    return fmaxf(mt, xor32(mt));
-  };
-
-  // Move the exponent offset only when some row grew by more than kRescaleTau.
-  auto maybe_rescale = [&](float mt) {
+    mt = fmaxf(mt, xor32(mt));
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
+      // Keep this a real (wave-uniform) branch: if the compiler speculates
+      // it into selects, every tile pays the multiply of the accumulator.
+      asm volatile("" ::: "memory");
       const float m_new = fmaxf(m_run, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -321,10 +400,6 @@ void fwd_kernel(FwdParams p) {
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
       m_run = m_new;
     }
-  };
-
-  // P~ = exp2(scaled score - m) rounded to bf16 pairs; fp32 row sums of P~.
-  auto exp_pack = [&](const f32x16 (&s)[KB], bf16x8 (&pb)[KB][2], bool prescaled) {
     const float neg_m = -m_run;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -334,8 +409,14 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 8 * t + 2 * i;
-          const float x0 = prescaled ? s[kb][r] + neg_m : __builtin_fmaf(s[kb][r], s2, neg_m);
-          const float x1 = prescaled ? s[kb][r + 1] + neg_m : __builtin_fmaf(s[kb][r + 1], s2, neg_m);
+          float x0, x1;
+          if constexpr (masked) {
+            x0 = s[kb][r] + neg_m;
+            x1 = s[kb][r + 1] + neg_m;
+          } else {
+            x0 = __builtin_fmaf(s[kb][r], s2, neg_m);
+            x1 = __builtin_fmaf(s[kb][r + 1], s2, neg_m);
+          }
           const float e0 = __builtin_amdgcn_exp2f(x0);
           const float e1 = __builtin_amdgcn_exp2f(x1);
           w[i] = pack_bf16(e0, e1);
@@ -346,70 +427,48 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  // O^T += V^T P^T for one tile.
-  auto pv = [&](const bf16x8 (&pb)[KB][2], int vbuf) {
-    const int base = (2 + vbuf) * TILE_BYTES;
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r0 = (32 * kb + 16 * t) * RB;
-          const v4i16 lo = lds_tr(base + r0 + v_rd[b]);
-          const v4i16 up = lds_tr(base + r0 + 8 * RB + v_rd[b]);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], o[b], 0, 0, 0);
-        }
-      }
+  auto softmax = [&](int kt) {
+    const int k0 = kt * BC;
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0))
+      softmax_tile(std::true_type{}, k0);
+    else
+      softmax_tile(std::false_type{}, k0);
+  };
+
+  auto active = [&](int kt) { return wave_has_rows && kt <= wave_last_kt; };
+
+  // ---- schedule ----
+  // Phase 2j   (group A) / 2j+1 (group B): M_j = [S^T_j, O^T += V^T_{j-1} P_{j-1}]
+  // Phase 2j+1 (group A) / 2j+2 (group B): V_j = softmax of tile j
+  // Group A copies K_{j+1} and V_j at the start of M_j and waits for them at
+  // the end of V_j, so they are in LDS before phase 2j+2 needs them. Buffer
+  // parity: K_t in K buf t&1, V_t in V buf t&1; the buffers written at phase
+  // 2j were last read at phase 2j-1.
+  if (!group_b) copy_k(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (group_b) barrier_nofence();          // run one phase behind group A
+  for (int j = 0; j <= n_kt; ++j) {
+    // ---- M phase ----
+    if (!group_b && j < n_kt) {
+      if (j + 1 < n_kt) copy_k(j + 1);
+      copy_v(j);
     }
-  };
-
-  // All of this thread's direct LDS copies have landed and every thread's are
-  // visible: wait for the memory counters, then the workgroup barrier.
-  auto tile_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-
-  // ---- prologue: K_0 -> Kbuf0, V_0 -> Vbuf0, K_1 -> Kbuf1, S_0 ----
-  copy_k(0, 0);
-  copy_v(0, 0);
-  if (n_kt > 1) copy_k(1, 1);
-  tile_sync();
-  f32x16 s_cur[KB];
-  if (wave_has_rows) qk(s_cur, 0);
-  __syncthreads();   // every wave is done with Kbuf0 before it is refilled
-
-  // ---- main loop: tile j's softmax and P V, tile j+1's S ----
-  for (int j = 0; j < n_kt; ++j) {
-    if (j + 2 < n_kt) copy_k(j + 2, j & 1);
-    if (j + 1 < n_kt) copy_v(j + 1, (j + 1) & 1);
-    const bool act_j = wave_has_rows && j <= wave_last_kt;
-    const bool act_j1 = wave_has_rows && j + 1 <= wave_last_kt;
-    f32x16 s_next[KB];
-    bf16x8 pb[KB][2];
-    const int k0 = j * BC;
-    const bool masked = need_mask(k0);
-    if (act_j && act_j1 && !masked) {
-      // Common case, one basic block: tile j+1's QK^T on the matrix cores
-      // alongside tile j's exponentials, then tile j's P V.
-      maybe_rescale(rowmax(s_cur, false, k0));
-      qk(s_next, (j + 1) & 1);
-      exp_pack(s_cur, pb, false);
-      pv(pb, j & 1);
+    const bool do_qk = j < n_kt && active(j);
+    const bool do_pv = j >= 1 && active(j - 1);
+    if (do_qk && do_pv) {
+      qk_pv(j);
     } else {
-      if (act_j1) qk(s_next, (j + 1) & 1);
-      if (act_j) {
-        maybe_rescale(rowmax(s_cur, masked, k0));
-        exp_pack(s_cur, pb, masked);
-        pv(pb, j & 1);
-      }
+      if (do_qk) qk(j);
+      if (do_pv) pv(j - 1);
     }
-    tile_sync();
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_next[kb];
+    barrier_nofence();
+    // ---- V phase ----
+    if (j < n_kt && active(j)) softmax(j);
+    if (!group_b) __builtin_amdgcn_s_waitcnt(0);   // this phase's copies have landed
+    barrier_nofence();
   }
+  if (!group_b) barrier_nofence();         // match group B's extra barrier
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
   const float l_tot = l_run + xor32(l_run);
