@@ -94,6 +94,7 @@ constexpr int kBC = 64;                   // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kRescaleTau = 8.0f;
+constexpr int kPrefetch = 4;              // MFMA-phase operand reads in flight
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -341,25 +342,46 @@ void fwd_kernel(FwdParams p) {
   // M phase with both products: the QK^T MFMAs of tile kt and the P V MFMAs
   // of tile kt-1 alternate, and each product walks its accumulators in turn
   // (S^T: 2 blocks, O^T: DB blocks), so consecutive MFMAs never depend on
-  // each other and the matrix pipe never waits for its own previous result.
+  // each other. Operands are read from LDS kPrefetch steps ahead into a small
+  // register ring, and sched_barrier keeps that order, so the MFMAs issue
+  // back to back instead of each waiting for the LDS read just before it.
   auto qk_pv = [&](int kt) {
-    constexpr int N = KB * DS;                   // == DB * KB * 2
+    constexpr int N = KB * DS;                   // steps; == DB * KB * 2
     static_assert(N == DB * KB * 2, "interleave");
+    constexpr int P = N < kPrefetch ? N : kPrefetch;
     const int kbase = (kt & 1) * TILE_BYTES;
     const int vbase = (2 + ((kt - 1) & 1)) * TILE_BYTES;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
+    auto k_frag = [&](int i) -> bf16x8 {
       const int ds = i / KB, kb = i % KB;
-      const bf16x8 a = lds_b128(kbase + 32 * kb * RB + k_rd[ds]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
+      return lds_b128(kbase + 32 * kb * RB + k_rd[ds]);
+    };
+    auto v_frag = [&](int i) -> bf16x8 {
       const int b = i % DB, c = i / DB, kb2 = c / 2, t = c % 2;
       const int r0 = (32 * kb2 + 16 * t) * RB;
       const v4i16 lo = lds_tr(vbase + r0 + v_rd[b]);
       const v4i16 up = lds_tr(vbase + r0 + 8 * RB + v_rd[b]);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb2][t], o[b], 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 kf[P], vf[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      kf[i] = k_frag(i);
+      vf[i] = v_frag(i);
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ds = i / KB, kb = i % KB;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % P], qr[ds], s[kb], 0, 0, 0);
+      const int b = i % DB, c = i / DB, kb2 = c / 2, t = c % 2;
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % P], pb[kb2][t], o[b], 0, 0, 0);
+      if (i + P < N) {
+        kf[i % P] = k_frag(i + P);
+        vf[i % P] = v_frag(i + P);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
