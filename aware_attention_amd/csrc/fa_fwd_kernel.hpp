@@ -17,13 +17,16 @@
 //
 // Two wave groups in ping-pong. Waves 0-3 (group A, rows 0-127) and waves 4-7
 // (group B, rows 128-255) share the four SIMDs of a CU, one wave of each
-// group per SIMD. Every tile is split into two phases that end at a
-// workgroup barrier:
-//   M phase (matrix cores): S^T of tile j, and O^T += V^T P^T of tile j-1;
-//   V phase (vector ALU):   the online softmax of tile j, giving P of tile j.
-// Group B runs one phase behind group A, so on every SIMD one wave issues
-// MFMAs while the other does exponentials: the softmax hides under the matrix
-// work without software pipelining inside a wave.
+// group per SIMD. Each key tile j is one period between workgroup barriers,
+// made of an M block (matrix cores: S^T of tile j, and O^T += V^T P^T of
+// tile j-1) and a V block (vector ALU: the online softmax of a tile):
+//   group A runs M_j, then the softmax of tile j;
+//   group B runs the softmax of tile j-1, then M_j.
+// So on every SIMD one wave issues MFMAs while the other does exponentials,
+// then they swap. There is no barrier between the two blocks: measured on
+// gfx950, a barrier at each block change restarts both waves of a SIMD in
+// step and serialises them, while free-running waves overlap their MFMA and
+// VALU work.
 //
 // Deferred rescaling. The running maximum m used as the exponent offset is
 // moved only when some row's tile maximum exceeds it by more than kRescaleTau
@@ -251,7 +254,7 @@ void fwd_kernel(FwdParams p) {
     k_src[n] = row * rs_bytes + ((phys ^ TL::k_swz(row)) * 16);
     v_src[n] = row * rs_bytes + ((phys ^ TL::v_swz(row)) * 16);
   }
-  auto copy_tile = [&](const uint8_t* gsrc, const int (&src)[NPW], int tile_base, int kt) {
+  auto copy_tile = [&](const uint8_t* gsrc, const int (&src)[NPW], int tile_base, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
     const uint8_t* g = gsrc + (int64_t)k0 * rs_bytes;
     const uint32_t lds0 = smem_lds + tile_base + gw * NPW * 1024;
@@ -270,8 +273,8 @@ void fwd_kernel(FwdParams p) {
       }
     }
   };
-  auto copy_k = [&](int kt) { copy_tile(kg, k_src, (kt & 1) * TILE_BYTES, kt); };
-  auto copy_v = [&](int kt) { copy_tile(vg, v_src, (2 + (kt & 1)) * TILE_BYTES, kt); };
+  auto copy_k = [&](int kt) __attribute__((always_inline)) { copy_tile(kg, k_src, (kt & 1) * TILE_BYTES, kt); };
+  auto copy_v = [&](int kt) __attribute__((always_inline)) { copy_tile(vg, v_src, (2 + (kt & 1)) * TILE_BYTES, kt); };
 
   // ---- LDS operand addresses of this lane ----
   // K operand (A of S^T = K Q^T): row 32*kb + l32, logical chunk 2*ds + hi.
@@ -289,10 +292,10 @@ void fwd_kernel(FwdParams p) {
   for (int b = 0; b < DB; ++b)
     v_rd[b] = v_row * RB + (((4 * b + v_x) ^ TL::v_swz(v_row)) * 16) + 8 * (vi & 1);
 
-  auto lds_b128 = [&](int byte) -> bf16x8 {
+  auto lds_b128 = [&](int byte) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(smem + byte);
   };
-  auto lds_tr = [&](int byte) -> v4i16 {
+  auto lds_tr = [&](int byte) __attribute__((always_inline)) -> v4i16 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint8_t*)smem + byte));
   };
@@ -307,7 +310,7 @@ void fwd_kernel(FwdParams p) {
   bf16x8 pb[KB][2];        // P~ of the previous tile, as MFMA B operands
 
   // S^T = K Q^T for one tile (BC keys x 32 queries).
-  auto qk = [&](int kt) {
+  auto qk = [&](int kt) __attribute__((always_inline)) {
     const int base = (kt & 1) * TILE_BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
@@ -321,7 +324,7 @@ void fwd_kernel(FwdParams p) {
     }
   };
   // O^T += V^T P^T for one tile.
-  auto pv = [&](int kt) {
+  auto pv = [&](int kt) __attribute__((always_inline)) {
     const int base = (2 + (kt & 1)) * TILE_BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -345,17 +348,17 @@ void fwd_kernel(FwdParams p) {
   // each other. Operands are read from LDS kPrefetch steps ahead into a small
   // register ring, and sched_barrier keeps that order, so the MFMAs issue
   // back to back instead of each waiting for the LDS read just before it.
-  auto qk_pv = [&](int kt) {
+  auto qk_pv = [&](int kt) __attribute__((always_inline)) {
     constexpr int N = KB * DS;                   // steps; == DB * KB * 2
     static_assert(N == DB * KB * 2, "interleave");
     constexpr int P = N < kPrefetch ? N : kPrefetch;
     const int kbase = (kt & 1) * TILE_BYTES;
     const int vbase = (2 + ((kt - 1) & 1)) * TILE_BYTES;
-    auto k_frag = [&](int i) -> bf16x8 {
+    auto k_frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
       const int ds = i / KB, kb = i % KB;
       return lds_b128(kbase + 32 * kb * RB + k_rd[ds]);
     };
-    auto v_frag = [&](int i) -> bf16x8 {
+    auto v_frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
       const int b = i % DB, c = i / DB, kb2 = c / 2, t = c % 2;
       const int r0 = (32 * kb2 + 16 * t) * RB;
       const v4i16 lo = lds_tr(vbase + r0 + v_rd[b]);
@@ -388,7 +391,7 @@ void fwd_kernel(FwdParams p) {
   // Online softmax of one tile: s -> pb, updating m_run, l_run and (rarely) o.
   // Instantiated separately for tiles that need the mask and tiles that do
   // not, so the common path carries no per-element selects.
-  auto softmax_tile = [&](auto masked_tag, int k0) {
+  auto softmax_tile = [&](auto masked_tag, int k0) __attribute__((always_inline)) {
     constexpr bool masked = decltype(masked_tag)::value;
     float mt = kNegInf;
     if constexpr (masked) {
@@ -449,7 +452,7 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  auto softmax = [&](int kt) {
+  auto softmax = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
     if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0))
       softmax_tile(std::true_type{}, k0);
@@ -457,25 +460,24 @@ void fwd_kernel(FwdParams p) {
       softmax_tile(std::false_type{}, k0);
   };
 
-  auto active = [&](int kt) { return wave_has_rows && kt <= wave_last_kt; };
+  auto active = [&](int kt) __attribute__((always_inline)) { return wave_has_rows && kt <= wave_last_kt; };
 
   // ---- schedule ----
-  // Phase 2j   (group A) / 2j+1 (group B): M_j = [S^T_j, O^T += V^T_{j-1} P_{j-1}]
-  // Phase 2j+1 (group A) / 2j+2 (group B): V_j = softmax of tile j
-  // Group A copies K_{j+1} and V_j at the start of M_j and waits for them at
-  // the end of V_j, so they are in LDS before phase 2j+2 needs them. Buffer
-  // parity: K_t in K buf t&1, V_t in V buf t&1; the buffers written at phase
-  // 2j were last read at phase 2j-1.
+  // One workgroup barrier per key tile. In period j (between barriers j-1
+  // and j):
+  //   group A: copies K(j+1), V(j); M_j = [S^T_j, O^T += V^T_{j-1} P_{j-1}];
+  //            V_j = softmax of tile j; waits for its copies;
+  //   group B: V_{j-1} = softmax of tile j-1; M_j.
+  // On every SIMD one wave starts with MFMAs while the other starts with
+  // exponentials, and the two then swap, with no barrier in between.
+  // LDS buffers: K_t in K buf t&1, V_t in V buf t&1. The buffers written in
+  // period j held K_{j-1} and V_{j-2}, last read in period j-1; the copies
+  // land (s_waitcnt by the issuing waves) before barrier j, ahead of their
+  // first readers in period j+1.
   if (!group_b) copy_k(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (group_b) barrier_nofence();          // run one phase behind group A
-  for (int j = 0; j <= n_kt; ++j) {
-    // ---- M phase ----
-    if (!group_b && j < n_kt) {
-      if (j + 1 < n_kt) copy_k(j + 1);
-      copy_v(j);
-    }
+  auto mfma_phase = [&](int j) __attribute__((always_inline)) {
     const bool do_qk = j < n_kt && active(j);
     const bool do_pv = j >= 1 && active(j - 1);
     if (do_qk && do_pv) {
@@ -484,13 +486,22 @@ void fwd_kernel(FwdParams p) {
       if (do_qk) qk(j);
       if (do_pv) pv(j - 1);
     }
-    barrier_nofence();
-    // ---- V phase ----
-    if (j < n_kt && active(j)) softmax(j);
-    if (!group_b) __builtin_amdgcn_s_waitcnt(0);   // this phase's copies have landed
+  };
+  for (int j = 0; j <= n_kt; ++j) {
+    if (!group_b) {
+      if (j < n_kt) {
+        if (j + 1 < n_kt) copy_k(j + 1);
+        copy_v(j);
+      }
+      mfma_phase(j);
+      if (j < n_kt && active(j)) softmax(j);
+      __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
+    } else {
+      if (j >= 1 && active(j - 1)) softmax(j - 1);
+      mfma_phase(j);
+    }
     barrier_nofence();
   }
-  if (!group_b) barrier_nofence();         // match group B's extra barrier
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
   const float l_tot = l_run + xor32(l_run);
