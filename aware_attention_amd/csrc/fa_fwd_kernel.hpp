@@ -42,12 +42,12 @@
 // Computing the transposed products puts one query per lane (n = l%32) in
 // both S^T and O^T, so the row statistics m, l and the rescale factor are
 // lane-local; the only cross-lane step per tile is one max exchange between
-// lane l and lane l^32. The accumulator registers of S^T feed the B operand
-// of the P V product directly, with no trip through LDS: register group
-// r = 8t..8t+7 of a 32-key block holds keys 16t + {0..3, 8..11} + 4*(l/32).
-// K and V sit in LDS row-major; the V^T operand comes from transposing 8-byte
-// reads (ds_read_b64_tr_b16), addressed so the transpose hands each lane the
-// keys in exactly that order.
+// lane l and lane l^32 (v_permlane32_swap). The accumulator registers of S^T
+// feed the B operand of the P V product directly, with no trip through LDS:
+// register group r = 8t..8t+7 of a 32-key block holds keys
+// 16t + {0..3, 8..11} + 4*(l/32). K and V sit in LDS row-major; the V^T
+// operand comes from transposing 8-byte reads (ds_read_b64_tr_b16),
+// addressed so the transpose hands each lane the keys in exactly that order.
 //
 // Masking ("FlashAttention/zh", section 變體與後續版本: causal masks):
 // keys past the sequence end and, when causal, keys after the query are set
@@ -100,6 +100,20 @@ constexpr float kRescaleTau = 8.0f;
 constexpr int kPrefetch = 4;              // MFMA-phase operand reads in flight
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max(x[l], x[l ^ 32]) in every lane l with one v_permlane32_swap, a VALU
+// op: it swaps the upper half of one copy of x with the lower half of
+// another, so each lane then holds x from both halves of the wave, whichever
+// half is swapped with which. Unlike a ds_bpermute it does not queue behind
+// the other wave group's LDS operand reads. Written as inline asm (the s_nop
+// covers the VALU-write-then-permlane-read hazard, which the compiler does
+// not see inside asm); the builtin was folded incorrectly by the compiler
+// when both operands were the same value.
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
 
 // max(a, b, c) in one v_max3_f32. Written as inline asm: the generic fmaxf
 // route quiets each MFMA result with an extra v_max before comparing, which
@@ -413,7 +427,7 @@ void fwd_kernel(FwdParams p) {
       }
       mt *= s2;
     }
-    mt = fmaxf(mt, xor32(mt));
+    mt = max_xor32(mt);
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
       // Keep this a real (wave-uniform) branch: if the compiler speculates
       // it into selects, every tile pays the multiply of the accumulator.
