@@ -137,19 +137,27 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
 // One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l's
-// 16 bytes from gptr land at LDS byte lds_base + 16*l (lds_base must be the
-// same in every lane of the wave). Issued as inline asm
-// on purpose: the compiler would otherwise treat every later LDS read as a
-// possible reader of this asynchronous write and wait for the copy to land
-// before it, even when (as here, by construction) the reads target another
-// buffer. The instruction has no register outputs; the kernel itself waits
-// for the copies (s_waitcnt vmcnt) before the barrier that publishes them.
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
+// 16 bytes from gbase + voff land at LDS byte lds_base + 16*l. gbase and
+// lds_base must be the same in every lane of the wave (they go to SGPRs and
+// M0); voff is the lane's unsigned 32-bit byte offset, so the per-lane
+// address needs no 64-bit arithmetic. Issued as inline asm on purpose: the
+// compiler would otherwise treat every later LDS read as a possible reader
+// of this asynchronous write and wait for the copy to land before it, even
+// when (as here, by construction) the reads target another buffer. The
+// instruction has no register outputs; the kernel itself waits for the
+// copies (s_waitcnt vmcnt) before the barrier that publishes them.
+__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  // readfirstlane returns a signed int: widen through uint32_t, or a low
+  // word with bit 31 set would be sign-extended over the high word.
+  const uint64_t b = reinterpret_cast<uint64_t>(gbase);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory", "m0");
 }
 
@@ -274,12 +282,12 @@ void fwd_kernel(FwdParams p) {
     const uint32_t lds0 = smem_lds + tile_base + gw * NPW * 1024;
     if (k0 + BC <= Nk) {
 #pragma unroll
-      for (int n = 0; n < NPW; ++n) copy16_to_lds(g + src[n], lds0 + n * 1024);
+      for (int n = 0; n < NPW; ++n) copy16_to_lds(g, (uint32_t)src[n], lds0 + n * 1024);
     } else {
 #pragma unroll
       for (int n = 0; n < NPW; ++n) {
         if (k0 + cp_row[n] < Nk) {
-          copy16_to_lds(g + src[n], lds0 + n * 1024);
+          copy16_to_lds(g, (uint32_t)src[n], lds0 + n * 1024);
         } else {
           *reinterpret_cast<u32x4*>(smem + tile_base + (gw * NPW + n) * 1024 + 16 * lane) =
               u32x4{0, 0, 0, 0};
