@@ -97,7 +97,7 @@ constexpr int kBC = 64;                   // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kRescaleTau = 8.0f;
-constexpr int kPrefetch = 4;              // MFMA-phase operand reads in flight
+constexpr int kPrefetch = 8;              // MFMA-phase operand fragments in flight
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -364,48 +364,48 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  // M phase with both products: the QK^T MFMAs of tile kt and the P V MFMAs
-  // of tile kt-1 alternate, and each product walks its accumulators in turn
-  // (S^T: 2 blocks, O^T: DB blocks), so consecutive MFMAs never depend on
-  // each other. Operands are read from LDS kPrefetch steps ahead into a small
-  // register ring, and sched_barrier keeps that order, so the MFMAs issue
-  // back to back instead of each waiting for the LDS read just before it.
+  // M phase with both products: the KB*DS QK^T MFMAs of tile kt, then the
+  // DB*KB*2 P V MFMAs of tile kt-1. Each product walks its accumulators in
+  // turn (S^T: KB blocks, O^T: DB blocks), so consecutive MFMAs never depend
+  // on each other. One register ring of kPrefetch operand fragments runs
+  // over both products, read from LDS that many MFMAs ahead, and
+  // sched_barrier keeps that order, so the MFMAs issue back to back instead
+  // of each waiting for its LDS read. (Measured on gfx950: this order with an
+  // 8-deep ring beats alternating QK and PV MFMAs with two 4-deep rings, at
+  // the same register count.)
   auto qk_pv = [&](int kt) __attribute__((always_inline)) {
-    constexpr int N = KB * DS;                   // steps; == DB * KB * 2
-    static_assert(N == DB * KB * 2, "interleave");
-    constexpr int P = N < kPrefetch ? N : kPrefetch;
+    constexpr int N = KB * DS;                   // MFMAs per product
+    static_assert(N == DB * KB * 2, "both products have the same length");
+    constexpr int R = 2 * N < kPrefetch ? 2 * N : kPrefetch;
     const int kbase = (kt & 1) * TILE_BYTES;
     const int vbase = (2 + ((kt - 1) & 1)) * TILE_BYTES;
-    auto k_frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-      const int ds = i / KB, kb = i % KB;
-      return lds_b128(kbase + 32 * kb * RB + k_rd[ds]);
-    };
-    auto v_frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-      const int b = i % DB, c = i / DB, kb2 = c / 2, t = c % 2;
-      const int r0 = (32 * kb2 + 16 * t) * RB;
+    auto frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      if (i < N) {   // K fragment of QK^T step i
+        const int ds = i / KB, kb = i % KB;
+        return lds_b128(kbase + 32 * kb * RB + k_rd[ds]);
+      }
+      const int ii = i - N, b = ii % DB, c = ii / DB, kb2 = c / 2, t = c % 2;
+      const int r0 = (32 * kb2 + 16 * t) * RB;   // V^T fragment of PV step ii
       const v4i16 lo = lds_tr(vbase + r0 + v_rd[b]);
       const v4i16 up = lds_tr(vbase + r0 + 8 * RB + v_rd[b]);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 kf[P], vf[P];
+    bf16x8 ring[R];
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      kf[i] = k_frag(i);
-      vf[i] = v_frag(i);
-    }
+    for (int i = 0; i < R; ++i) ring[i] = frag(i);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int ds = i / KB, kb = i % KB;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % P], qr[ds], s[kb], 0, 0, 0);
-      const int b = i % DB, c = i / DB, kb2 = c / 2, t = c % 2;
-      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % P], pb[kb2][t], o[b], 0, 0, 0);
-      if (i + P < N) {
-        kf[i % P] = k_frag(i + P);
-        vf[i % P] = v_frag(i + P);
+    for (int i = 0; i < 2 * N; ++i) {
+      if (i < N) {
+        const int ds = i / KB, kb = i % KB;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % R], qr[ds], s[kb], 0, 0, 0);
+      } else {
+        const int ii = i - N, b = ii % DB, c = ii / DB, kb2 = c / 2, t = c % 2;
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % R], pb[kb2][t], o[b], 0, 0, 0);
       }
+      if (i + R < 2 * N) ring[i % R] = frag(i + R);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -509,7 +509,14 @@ void fwd_kernel(FwdParams p) {
       if (do_pv) pv(j - 1);
     }
   };
-  for (int j = 0; j <= n_kt; ++j) {
+  // Steady periods: j in [1, j_steady) where, for every wavefront of the
+  // workgroup, tiles j-1 and j are full, unmasked and active, and K(j+1) is a
+  // full tile. They run without any of the per-tile tests. The bound is the
+  // same in every wave, so all waves cross the same barriers.
+  const int full_kt = Nk / BC;                         // tiles with BC keys
+  const int unmasked_kt = CAUSAL ? min(full_kt, q0 / BC) : full_kt;
+  const int j_steady = (q0 + kBR <= Nq) ? max(1, min(unmasked_kt, full_kt - 1)) : 1;
+  auto period = [&](int j) __attribute__((always_inline)) {
     if (!group_b) {
       if (j < n_kt) {
         if (j + 1 < n_kt) copy_k(j + 1);
@@ -523,7 +530,28 @@ void fwd_kernel(FwdParams p) {
       mfma_phase(j);
     }
     barrier_nofence();
+  };
+  period(0);
+  for (int j = 1; j < j_steady; ++j) {
+    if (!group_b) {
+      const uint8_t* gk = kg + (int64_t)((j + 1) * BC) * rs_bytes;
+      const uint8_t* gv = vg + (int64_t)(j * BC) * rs_bytes;
+      const uint32_t lk = smem_lds + ((j + 1) & 1) * TILE_BYTES + gw * NPW * 1024;
+      const uint32_t lv = smem_lds + (2 + (j & 1)) * TILE_BYTES + gw * NPW * 1024;
+#pragma unroll
+      for (int n = 0; n < NPW; ++n) copy16_to_lds(gk, (uint32_t)k_src[n], lk + n * 1024);
+#pragma unroll
+      for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
+      qk_pv(j);
+      softmax_tile(std::false_type{}, 0);
+      __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
+    } else {
+      softmax_tile(std::false_type{}, 0);
+      qk_pv(j);
+    }
+    barrier_nofence();
   }
+  for (int j = j_steady; j <= n_kt; ++j) period(j);
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
   const float l_tot = l_run + xor32(l_run);
