@@ -179,9 +179,13 @@ struct TileLayout {
   }
 };
 
+// Occupancy: two waves per SIMD (one workgroup per CU) at d = 64 and 128,
+// where the per-lane state needs up to 256 VGPRs. At d = 32 the state fits
+// in 128 VGPRs, so two workgroups share a CU (four waves per SIMD): the
+// softmax dominates there, and the extra waves hide its latency.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(2, 2)))
+                          amdgpu_waves_per_eu(D == 32 ? 4 : 2, D == 32 ? 4 : 2)))
 void fwd_kernel(FwdParams p) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
   constexpr int BC = kBC;
