@@ -214,10 +214,30 @@ void fwd_kernel(FwdParams p) {
   const int gw = wave & 3;               // wave index inside its group
 
   // ---- work item: (query tile, head, batch or sequence) ----
-  const int per_qt = p.H * p.nbatch;
-  int qt = blockIdx.x / per_qt;
-  const int rem = blockIdx.x - qt * per_qt;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // longest rows of the mask first
+  // A unit is one (batch or sequence, head): all its query tiles read the
+  // same K and V. Workgroups go to the 8 XCDs round-robin by blockIdx.x, and
+  // each XCD has its own L2.
+  //  * Unmasked attention, unit count a multiple of 8: blockIdx.x = 8m + x
+  //    maps XCD x's m-th workgroup to unit x + 8 * (m / n_qtiles), query tile
+  //    m % n_qtiles, so an XCD works through the query tiles of a few units
+  //    at a time and they share K/V tiles in its L2 (ViT-shaped batch: HBM
+  //    reads 2.3 GB -> 0.64 GB per launch, +15 %).
+  //  * Otherwise, and always for causal attention, tile-major: blockIdx.x =
+  //    rank * units + unit. With a unit count that is a multiple of 8 each
+  //    XCD still sees only units congruent to its index; causal ranks run
+  //    longest rows of the mask first, across all units, which balances the
+  //    CUs (unit-grouped causal order measured 2-12 % slower).
+  const int per_qt = p.H * p.nbatch;   // units
+  int qt, rem;
+  if (!CAUSAL && (per_qt & 7) == 0) {
+    const int m = blockIdx.x >> 3;
+    qt = m % p.n_qtiles;
+    rem = (blockIdx.x & 7) + 8 * (m / p.n_qtiles);
+  } else {
+    qt = blockIdx.x / per_qt;
+    rem = blockIdx.x - qt * per_qt;
+  }
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;
   const int head = rem % p.H;
   const int bidx = rem / p.H;
 
