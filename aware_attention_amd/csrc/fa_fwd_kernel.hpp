@@ -396,8 +396,10 @@ void fwd_kernel(FwdParams p) {
   // sched_barrier keeps that order, so the MFMAs issue back to back instead
   // of each waiting for its LDS read. (Measured on gfx950: this order with an
   // 8-deep ring beats alternating QK and PV MFMAs with two 4-deep rings, at
-  // the same register count.)
-  auto qk_pv = [&](int kt) __attribute__((always_inline)) {
+  // the same register count.) `between` runs after the ring's first reads
+  // are issued and before the first MFMA (group A issues its HBM -> LDS
+  // copies there, which hides the first reads' latency behind them).
+  auto qk_pv = [&](int kt, auto&& between) __attribute__((always_inline)) {
     constexpr int N = KB * DS;                   // MFMAs per product
     static_assert(N == DB * KB * 2, "both products have the same length");
     constexpr int R = 2 * N < kPrefetch ? 2 * N : kPrefetch;
@@ -417,6 +419,8 @@ void fwd_kernel(FwdParams p) {
     bf16x8 ring[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) ring[i] = frag(i);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
     __builtin_amdgcn_sched_barrier(0);
@@ -527,7 +531,7 @@ void fwd_kernel(FwdParams p) {
     const bool do_qk = j < n_kt && active(j);
     const bool do_pv = j >= 1 && active(j - 1);
     if (do_qk && do_pv) {
-      qk_pv(j);
+      qk_pv(j, [] {});
     } else {
       if (do_qk) qk(j);
       if (do_pv) pv(j - 1);
@@ -562,16 +566,17 @@ void fwd_kernel(FwdParams p) {
       const uint8_t* gv = vg + (int64_t)(j * BC) * rs_bytes;
       const uint32_t lk = smem_lds + ((j + 1) & 1) * TILE_BYTES + gw * NPW * 1024;
       const uint32_t lv = smem_lds + (2 + (j & 1)) * TILE_BYTES + gw * NPW * 1024;
+      qk_pv(j, [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int n = 0; n < NPW; ++n) copy16_to_lds(gk, (uint32_t)k_src[n], lk + n * 1024);
+        for (int n = 0; n < NPW; ++n) copy16_to_lds(gk, (uint32_t)k_src[n], lk + n * 1024);
 #pragma unroll
-      for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
-      qk_pv(j);
+        for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
+      });
       softmax_tile(std::false_type{}, 0);
       __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
     } else {
       softmax_tile(std::false_type{}, 0);
-      qk_pv(j);
+      qk_pv(j, [] {});
     }
     barrier_nofence();
   }

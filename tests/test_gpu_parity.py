@@ -1,6 +1,6 @@
 """HIP path vs the float64 CPU oracle, element by element, on seeded inputs.
 
-Small cases compare every output; they span several 128-row query tiles and
+Small cases compare every output; they span several 256-row query tiles and
 64-key tiles and end on ragged tails. The full-size workloads compare sampled
 (batch, head) pairs and rows that the oracle computes one by one, plus a
 property that holds at any size (each output row is a convex combination of
@@ -77,6 +77,27 @@ def test_detector_400_full():
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_rows_several_tiles(d, causal):
     check_dense_full(1, 700, 700, 2, d, causal, seed=3000 + d + causal)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_unit_grouped_order(d):
+    # Unmasked with a unit count (batch x heads) that is a multiple of 8: the
+    # kernel numbers query tiles unit by unit. Three query tiles per unit, the
+    # last one ragged.
+    check_dense_full(2, 600, 600, 4, d, False, seed=5000 + d)
+
+
+def test_varlen_unit_grouped_order():
+    # Unmasked varlen with 4 sequences x 2 heads = 8 units, one sequence longer
+    # than two query tiles and one of a single row.
+    torch_or_skip()
+    lengths = [600, 1, 300, 257]
+    say(f"varlen lengths={lengths} d=64 causal=False H=2")
+    q, k, v, cu = W.make_varlen(lengths, 2, 64, seed=5100)
+    og, lg = run_varlen(q, k, v, cu, max(lengths), 0.125, False)
+    oref, lref = attention_varlen(to_f64(q), to_f64(k), to_f64(v), cu, 0.125, False)
+    assert_o_close(og, oref, "O")
+    assert_l_close(lg, lref, "L")
 
 
 def test_rms_normalised_qk():
