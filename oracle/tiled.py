@@ -20,9 +20,12 @@ Attention v2，提速原理浅析" (section 3.2): the block's exponentials are t
 against the new running maximum directly, l_new = l_old e^{m_old - m_new} +
 sum e^{s - m_new}. The two are equal in exact arithmetic.
 
-Reading where the pages are silent: with a causal mask a block can be fully
-masked for some rows (m_ij = -inf). Such a row's block contributes nothing:
-its exponentials are 0 and its merge factor e^{m_ij - m_new} is taken as 0.
+Reading where the pages are silent: with a causal or banded mask a block can
+be fully masked for some rows (m_ij = -inf). Such a row's block contributes
+nothing: its exponentials are 0 and its merge factor e^{m_ij - m_new} is taken
+as 0. A row that sees no key at all ends with l = 0; its output is 0 and
+L = -inf. The band (window = (left, right)) is the one attention.py defines:
+query i sees key j iff i + off - left <= j <= i + off + right, off = Nk - Nq.
 """
 from __future__ import annotations
 
@@ -30,7 +33,8 @@ import numpy as np
 
 
 def attention_tiled(q, k, v, scale: float, causal: bool = False,
-                    block_rows: int = 16, block_cols: int = 16, form: str = "local"):
+                    block_rows: int = 16, block_cols: int = 16, form: str = "local",
+                    window=None):
     """One head, blockwise. Returns (O (Nq,dv), L (Nq,)) in float64."""
     if form not in ("local", "running"):
         raise ValueError(form)
@@ -51,10 +55,15 @@ def attention_tiled(q, k, v, scale: float, causal: bool = False,
         for c0 in range(0, Nk, block_cols):
             c1 = min(c0 + block_cols, Nk)
             Sij = scale * (Qi @ k[c0:c1].T)
+            rows = np.arange(r0, r1)[:, None]
+            cols = np.arange(c0, c1)[None, :]
             if causal:
-                rows = np.arange(r0, r1)[:, None]
-                cols = np.arange(c0, c1)[None, :]
                 Sij = np.where(cols > rows, -np.inf, Sij)
+            if window is not None:
+                left, right = window
+                lo = rows + (Nk - Nq) - (left if left is not None else Nk + Nq)
+                hi = rows + (Nk - Nq) + (right if right is not None else Nk + Nq)
+                Sij = np.where((cols < lo) | (cols > hi), -np.inf, Sij)
             mij = Sij.max(axis=1)
             m_new = np.maximum(mi, mij)
             # e^{m_i - m_new}; a row that has seen nothing yet has O_i = l_i = 0.
@@ -73,6 +82,8 @@ def attention_tiled(q, k, v, scale: float, causal: bool = False,
                 Oi = Oi * alpha[:, None] + Pij @ v[c0:c1]
                 li = li * alpha + Pij.sum(axis=1)
             mi = m_new
-        O[r0:r1] = Oi / li[:, None]
-        L[r0:r1] = mi + np.log(li)
+        empty = li == 0
+        O[r0:r1] = Oi / np.where(empty, 1.0, li)[:, None]
+        with np.errstate(divide="ignore"):
+            L[r0:r1] = np.where(empty, -np.inf, mi + np.log(np.where(empty, 1.0, li)))
     return O, L

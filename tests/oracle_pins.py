@@ -245,3 +245,125 @@ def pin_golden(fn):
 ALL_PINS = [pin_brute_force, pin_tiled_agrees, pin_probability_rows, pin_zero_query,
             pin_constant_v, pin_single_key, pin_key_permutation, pin_key_shift,
             pin_library, pin_golden]
+
+
+# ---------------------------------------------------------------------------
+# Banded mask. fn(q, k, v, scale, window) -> (O, L), window = (left, right),
+# None = unbounded; query i sees key j iff i+off-left <= j <= i+off+right with
+# off = Nk - Nq; a row that sees no key gives O = 0 and L = -inf.
+# ---------------------------------------------------------------------------
+
+def _close_inf(a, b, tol, what):
+    """Like _close, but -inf entries must match exactly (position and sign)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    assert not np.any(np.isnan(a)), f"{what}: NaN values"
+    ia, ib = np.isneginf(a), np.isneginf(b)
+    assert np.array_equal(ia, ib), f"{what}: -inf pattern differs"
+    assert np.all(np.isfinite(a[~ia])), f"{what}: non-finite values"
+    err = np.max(np.abs(a[~ia] - b[~ib])) if np.any(~ia) else 0.0
+    assert err <= tol, f"{what}: max abs err {err} > {tol}"
+
+
+def brute_force_band(q, k, v, scale, window):
+    """Pure-Python loops: the band test written out per (i, j) pair."""
+    Nq, Nk = len(q), len(k)
+    left, right = window
+    off = Nk - Nq
+    O, L = [], []
+    for i in range(Nq):
+        w = []
+        for j in range(Nk):
+            if left is not None and j - (i + off) < -left:
+                continue
+            if right is not None and j - (i + off) > right:
+                continue
+            s = scale * math.fsum(q[i][t] * k[j][t] for t in range(len(q[i])))
+            w.append((math.exp(s), j))
+        if not w:
+            O.append([0.0] * len(v[0]))
+            L.append(-math.inf)
+            continue
+        Z = math.fsum(e for e, _ in w)
+        O.append([math.fsum(e * v[j][c] for e, j in w) / Z for c in range(len(v[0]))])
+        L.append(math.log(Z))
+    return O, L
+
+
+_WINDOWS = [(None, None), (None, 0), (0, 0), (1, 0), (0, 2), (2, 1), (3, None), (None, 1), (5, 5)]
+
+
+def pin_band_brute_force(fn):
+    rng = _rng(131)
+    for Nq in (1, 3, 5, 8):
+        for Nk in (1, 2, 5, 8):
+            for window in _WINDOWS:
+                q = rng.standard_normal((Nq, 3))
+                k = rng.standard_normal((Nk, 3))
+                v = rng.standard_normal((Nk, 2))
+                scale = float(rng.uniform(0.2, 1.5))
+                O, L = fn(q, k, v, scale, window)
+                Ob, Lb = brute_force_band(q.tolist(), k.tolist(), v.tolist(), scale, window)
+                what = f"band {window} Nq={Nq} Nk={Nk}"
+                _close(O, Ob, 1e-12, "O " + what)
+                _close_inf(L, Lb, 1e-12, "L " + what)
+
+
+def pin_band_reduces(fn):
+    """(None, None) is unmasked attention and (None, 0) with Nq == Nk is causal
+    attention, both checked against the plain brute force above."""
+    rng = _rng(137)
+    for N in (1, 4, 9):
+        for Nk in (N, 6):
+            q = rng.standard_normal((N, 4))
+            k = rng.standard_normal((Nk, 4))
+            v = rng.standard_normal((Nk, 3))
+            O, L = fn(q, k, v, 0.7, (None, None))
+            Ob, Lb = brute_force(q.tolist(), k.tolist(), v.tolist(), 0.7, False)
+            _close(O, Ob, 1e-12, f"O unbounded band N={N} Nk={Nk}")
+            _close(L, Lb, 1e-12, f"L unbounded band N={N} Nk={Nk}")
+        k = rng.standard_normal((N, 4))
+        v = rng.standard_normal((N, 3))
+        O, L = fn(q, k, v, 0.7, (None, 0))
+        Ob, Lb = brute_force(q.tolist(), k.tolist(), v.tolist(), 0.7, True)
+        _close(O, Ob, 1e-12, f"O causal band N={N}")
+        _close(L, Lb, 1e-12, f"L causal band N={N}")
+
+
+def pin_band_diagonal(fn):
+    """Band (0, 0): query i sees only key i + off, so O_i = v_{i+off} and
+    L_i = scale q_i . k_{i+off}; outside [0, Nk) the row is empty."""
+    rng = _rng(139)
+    for Nq, Nk in ((5, 5), (3, 7), (7, 3)):
+        q = rng.standard_normal((Nq, 4))
+        k = rng.standard_normal((Nk, 4))
+        v = rng.standard_normal((Nk, 2))
+        O, L = fn(q, k, v, 0.9, (0, 0))
+        off = Nk - Nq
+        for i in range(Nq):
+            j = i + off
+            if 0 <= j < Nk:
+                _close(O[i], v[j], 1e-12, f"O diagonal band row {i}")
+                _close([L[i]], [0.9 * float(q[i] @ k[j])], 1e-12, f"L diagonal band row {i}")
+            else:
+                _close(O[i], np.zeros(2), 0.0, f"O empty row {i}")
+                assert L[i] == -math.inf, f"L empty row {i}: {L[i]}"
+
+
+def pin_band_tiled_agrees(fn):
+    from oracle.tiled import attention_tiled
+    rng = _rng(149)
+    for Nq, Nk in ((20, 20), (13, 29), (29, 13)):
+        q = rng.standard_normal((Nq, 5))
+        k = rng.standard_normal((Nk, 5))
+        v = rng.standard_normal((Nk, 3))
+        for window in ((None, 0), (4, 3), (0, 6), (7, None)):
+            O, L = fn(q, k, v, 0.6, window)
+            for br, bc, form in ((1, 1, "local"), (4, 3, "local"), (16, 16, "running")):
+                Ot, Lt = attention_tiled(q, k, v, 0.6, False, br, bc, form, window=window)
+                _close(O, Ot, 1e-12, f"O tiled band {window} {br}x{bc} {form}")
+                _close_inf(L, Lt, 1e-12, f"L tiled band {window} {br}x{bc} {form}")
+
+
+BAND_PINS = [pin_band_brute_force, pin_band_reduces, pin_band_diagonal, pin_band_tiled_agrees]

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from oracle import attention, attention_dense, attention_probs, attention_tiled, attention_varlen
-from tests.oracle_pins import ALL_PINS
+from tests.oracle_pins import ALL_PINS, BAND_PINS
 
 
 def _tiled_fn(q, k, v, scale, causal):
@@ -21,6 +21,26 @@ def test_oracle_definition_pins(pin):
 def test_oracle_tiled_pins(pin):
     """The blockwise algorithm meets the same pins on its own."""
     pin(_tiled_fn)
+
+
+@pytest.mark.parametrize("pin", BAND_PINS, ids=lambda p: p.__name__)
+def test_oracle_band_pins(pin):
+    pin(lambda q, k, v, scale, window: attention(q, k, v, scale, window=window))
+
+
+@pytest.mark.parametrize("pin", BAND_PINS, ids=lambda p: p.__name__)
+def test_oracle_tiled_band_pins(pin):
+    pin(lambda q, k, v, scale, window: attention_tiled(q, k, v, scale, False, 4, 3, window=window))
+
+
+def test_band_probs_rows_sum_to_one_or_zero():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((7, 4))
+    k = rng.standard_normal((11, 4))
+    P = attention_probs(q, k, 0.5, window=(1, 0))
+    sums = P.sum(1)
+    assert np.all((np.abs(sums - 1.0) < 1e-14) | (sums == 0.0))
+    assert np.all(P >= 0)
 
 
 def test_probs_match_attention_weights():

@@ -83,3 +83,73 @@ def test_mutation_is_caught(mutation):
         except Exception:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {mutation!r}"
+
+
+# ---------------------------------------------------------------------------
+# Banded mask: planted mistakes in a copy of the band logic must each fail at
+# least one of the band pins.
+# ---------------------------------------------------------------------------
+
+from tests.oracle_pins import BAND_PINS  # noqa: E402
+
+BAND_MUTATIONS = ["left_off_by_one", "right_off_by_one", "alignment_flipped",
+                  "alignment_ignored", "empty_row_nan", "empty_row_l_zero",
+                  "window_sides_swapped"]
+
+
+def _make_band(mutation):
+    def fn(q, k, v, scale, window):
+        q = np.asarray(q, dtype=np.float64)
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        Nq, Nk = q.shape[0], k.shape[0]
+        left, right = window
+        if mutation == "window_sides_swapped":
+            left, right = right, left
+        off = Nk - Nq
+        if mutation == "alignment_flipped":
+            off = Nq - Nk
+        elif mutation == "alignment_ignored":
+            off = 0
+        i = np.arange(Nq)[:, None] + off
+        j = np.arange(Nk)[None, :]
+        vis = np.ones((Nq, Nk), dtype=bool)
+        if left is not None:
+            vis &= j >= i - left + (1 if mutation == "left_off_by_one" else 0)
+        if right is not None:
+            vis &= j <= i + right - (1 if mutation == "right_off_by_one" else 0)
+        S = np.where(vis, scale * (q @ k.T), -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        if mutation != "empty_row_nan":
+            m = np.where(np.isfinite(m), m, 0.0)
+        e = np.exp(S - m)
+        l = e.sum(axis=1, keepdims=True)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            if mutation == "empty_row_nan":
+                O = (e / l) @ v
+                L = m[:, 0] + np.log(l[:, 0])
+            else:
+                O = (e / np.where(l > 0, l, 1.0)) @ v
+                L = np.where(l[:, 0] > 0, m[:, 0] + np.log(np.where(l > 0, l, 1.0)[:, 0]),
+                             0.0 if mutation == "empty_row_l_zero" else -np.inf)
+        return O, L
+    return fn
+
+
+def test_band_reference_copy_passes():
+    """The unmutated copy passes every band pin (so the mutants fail for their mistake)."""
+    fn = _make_band("none")
+    for pin in BAND_PINS:
+        pin(fn)
+
+
+@pytest.mark.parametrize("mutation", BAND_MUTATIONS)
+def test_band_mutant_is_caught(mutation):
+    fn = _make_band(mutation)
+    failed = []
+    for pin in BAND_PINS:
+        try:
+            pin(fn)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(pin.__name__)
+    assert failed, f"band mutation {mutation!r} passed every band pin"
