@@ -11,6 +11,10 @@ library is missing or the device is not a gfx950, calls raise.
     o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=False)
         q/k/v (total,H,d), cu_seqlens int32 (num_seqs+1,) on the device ->
         o (total,H,d), lse (H,total).
+    Both take window=(left, right) instead of causal for a banded mask: query i
+    sees key j iff i + (Nk - Nq) - left <= j <= i + (Nk - Nq) + right (varlen:
+    offset 0), None meaning no bound on that side; rows that see no key get
+    o = 0 and lse = -inf (entry points fa_fwd_band / fa_fwd_varlen_band).
 
 The default scale is 1/sqrt(d), as in the definition on "FlashAttention/zh"
 (marovi.ai wiki), section 為何標準注意力運行緩慢. Only half precision on the
@@ -23,7 +27,8 @@ from __future__ import annotations
 import math
 
 from ._lib import (FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_OK, FaError,
-                   check, load, raw_fa_fwd, raw_fa_fwd_varlen)
+                   check, load, raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_varlen,
+                   raw_fa_fwd_varlen_band)
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "FaError", "load", "FA_OK", "FA_ERR_INVALID_ARGUMENT",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
@@ -52,7 +57,18 @@ def _scale(softmax_scale, d):
     return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
 
 
-def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None):
+def _window(window, causal):
+    """(left, right) with None for unbounded -> the ABI's ints (-1 = unbounded)."""
+    if causal:
+        raise ValueError("pass either causal=True or window, not both (causal is window=(None, 0))")
+    left, right = window
+    sides = tuple(-1 if w is None else int(w) for w in (left, right))
+    if any(w is not None and int(w) < 0 for w in (left, right)):
+        raise ValueError("window sides must be >= 0, or None for unbounded")
+    return tuple(min(w, 2**31 - 1) for w in sides)
+
+
+def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, window=None):
     """Attention forward over an equal-length batch; returns (o, lse)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -73,13 +89,20 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None):
         raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, Nq)")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        check(raw_fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                         B, Nq, Nk, H, d, _scale(softmax_scale, d), int(bool(causal)), stream))
+        if window is None:
+            check(raw_fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, Nq, Nk, H, d, _scale(softmax_scale, d),
+                             int(bool(causal)), stream))
+        else:
+            wl, wr = _window(window, causal)
+            check(raw_fa_fwd_band(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), B, Nq, Nk, H, d, _scale(softmax_scale, d),
+                                  wl, wr, stream))
     return out, lse
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=False,
-                  out=None, lse=None):
+                  out=None, lse=None, window=None):
     """Attention forward over a packed variable-length batch; returns (o, lse)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -101,7 +124,15 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=Fa
         raise ValueError("lse must be a contiguous float32 tensor of shape (H, total)")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        check(raw_fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                lse.data_ptr(), cu_seqlens.data_ptr(), num_seqs, int(max_seqlen),
-                                total, H, d, _scale(softmax_scale, d), int(bool(causal)), stream))
+        if window is None:
+            check(raw_fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), cu_seqlens.data_ptr(), num_seqs,
+                                    int(max_seqlen), total, H, d, _scale(softmax_scale, d),
+                                    int(bool(causal)), stream))
+        else:
+            wl, wr = _window(window, causal)
+            check(raw_fa_fwd_varlen_band(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(),
+                                         num_seqs, int(max_seqlen), total, H, d,
+                                         _scale(softmax_scale, d), wl, wr, stream))
     return out, lse

@@ -14,7 +14,8 @@ FA_ERR_INVALID_ARGUMENT = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_status_string", "fa_last_error", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_status_string",
+            "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -41,6 +42,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i32
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_varlen.restype = i32
+    lib.fa_fwd_band.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.fa_fwd_band.restype = i32
+    lib.fa_fwd_varlen_band.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                       i32, vp]
+    lib.fa_fwd_varlen_band.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -69,3 +75,17 @@ def raw_fa_fwd_varlen(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d, sc
     """Pointer-level call of fa_fwd_varlen; returns the status code."""
     return load().fa_fwd_varlen(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d,
                                 scale, causal, stream)
+
+
+def raw_fa_fwd_band(q, k, v, o, lse, B, Nq, Nk, H, d, scale, window_left, window_right,
+                    stream) -> int:
+    """Pointer-level call of fa_fwd_band; returns the status code."""
+    return load().fa_fwd_band(q, k, v, o, lse, B, Nq, Nk, H, d, scale, window_left,
+                              window_right, stream)
+
+
+def raw_fa_fwd_varlen_band(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d, scale,
+                           window_left, window_right, stream) -> int:
+    """Pointer-level call of fa_fwd_varlen_band; returns the status code."""
+    return load().fa_fwd_varlen_band(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d,
+                                     scale, window_left, window_right, stream)

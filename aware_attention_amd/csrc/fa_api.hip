@@ -53,23 +53,48 @@ fa_status check_device() {
   return FA_OK;
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool BAND>
 hipError_t launch_one(const fa::FwdParams& p, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(fa::kThreads),
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN, BAND>), dim3(grid), dim3(fa::kThreads),
                      0, stream, p);
   return hipGetLastError();
 }
 
-template <bool VARLEN>
-hipError_t launch(const fa::FwdParams& p, int d, bool causal, uint32_t grid, hipStream_t stream) {
-  switch (d) {
-    case 32: return causal ? launch_one<32, true, VARLEN>(p, grid, stream)
-                           : launch_one<32, false, VARLEN>(p, grid, stream);
-    case 64: return causal ? launch_one<64, true, VARLEN>(p, grid, stream)
-                           : launch_one<64, false, VARLEN>(p, grid, stream);
-    default: return causal ? launch_one<128, true, VARLEN>(p, grid, stream)
-                           : launch_one<128, false, VARLEN>(p, grid, stream);
+// Mask of a launch: none, causal (top-left, Nq == Nk) or a band.
+enum class Mask { kNone, kCausal, kBand };
+
+template <int D, bool VARLEN>
+hipError_t launch_d(const fa::FwdParams& p, Mask mask, uint32_t grid, hipStream_t stream) {
+  switch (mask) {
+    case Mask::kCausal: return launch_one<D, true, VARLEN, false>(p, grid, stream);
+    case Mask::kBand: return launch_one<D, false, VARLEN, true>(p, grid, stream);
+    default: return launch_one<D, false, VARLEN, false>(p, grid, stream);
   }
+}
+
+template <bool VARLEN>
+hipError_t launch(const fa::FwdParams& p, int d, Mask mask, uint32_t grid, hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_d<32, VARLEN>(p, mask, grid, stream);
+    case 64: return launch_d<64, VARLEN>(p, mask, grid, stream);
+    default: return launch_d<128, VARLEN>(p, mask, grid, stream);
+  }
+}
+
+// Window sides: >= 0, or -1 for unbounded. A side of max(nq, nk) already
+// reaches every key (left needs Nk - 1 at most, right Nq - 1), so -1 and any
+// larger side are passed to the kernel as max(nq, nk); with sequences of at
+// most kMaxBandLen the kernel's 32-bit band bounds (about 3 max(nq, nk)) stay
+// in range.
+constexpr int64_t kMaxBandLen = int64_t{1} << 29;
+fa_status check_window(int32_t left, int32_t right) {
+  if (left < -1 || right < -1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window sides must be >= 0, or -1 for unbounded");
+  return FA_OK;
+}
+int32_t window_side(int32_t w, int64_t nq, int64_t nk) {
+  const int64_t unbounded = nq > nk ? nq : nk;
+  return (int32_t)((w < 0 || w > unbounded) ? unbounded : w);
 }
 
 fa_status check_common(int32_t H, int32_t d, float scale, int32_t causal) {
@@ -83,19 +108,18 @@ fa_status check_common(int32_t H, int32_t d, float scale, int32_t causal) {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
-                 float softmax_scale, int32_t causal, void* stream) {
-  g_last_error.clear();
+// Equal-length batch; the arguments other than the mask are those of fa_fwd.
+fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                    float softmax_scale, int32_t causal, Mask mask, int32_t win_left,
+                    int32_t win_right, void* stream) {
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (B < 1 || Nq < 1 || Nk < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B, Nq and Nk must be >= 1");
   fa_status st = check_common(H, d, softmax_scale, causal);
   if (st != FA_OK) return st;
   if (causal && Nq != Nk) return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
+  if (mask == Mask::kBand && (Nq > kMaxBandLen || Nk > kMaxBandLen))
+    return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const int64_t n_qt = (Nq + fa::kBR - 1) / fa::kBR;
@@ -122,22 +146,29 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.nbatch = B;
   p.n_qtiles = (int32_t)n_qt;
   p.scale_log2 = softmax_scale * kLog2e;
-  hipError_t e = launch<false>(p, d, causal != 0, (uint32_t)grid, static_cast<hipStream_t>(stream));
+  p.win_left = window_side(win_left, Nq, Nk);
+  p.win_right = window_side(win_right, Nq, Nk);
+  p.band_off = Nk - Nq;
+  hipError_t e = launch<false>(p, d, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
 }
 
-fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
-                        int32_t total, int32_t H, int32_t d, float softmax_scale,
-                        int32_t causal, void* stream) {
-  g_last_error.clear();
+// Packed variable-length batch; the arguments other than the mask are those
+// of fa_fwd_varlen.
+fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                     int32_t total, int32_t H, int32_t d, float softmax_scale,
+                     int32_t causal, Mask mask, int32_t win_left, int32_t win_right,
+                     void* stream) {
   if (!cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
   if (num_seqs < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
   if (total < 0 || max_seqlen < 0) return fail(FA_ERR_INVALID_ARGUMENT, "total and max_seqlen must be >= 0");
   if (max_seqlen > total) return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen exceeds total");
   fa_status st = check_common(H, d, softmax_scale, causal);
   if (st != FA_OK) return st;
+  if (mask == Mask::kBand && max_seqlen > kMaxBandLen)
+    return fail(FA_ERR_UNSUPPORTED, "banded attention supports max_seqlen <= 2^29");
   if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
@@ -167,9 +198,56 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   p.nbatch = num_seqs;
   p.n_qtiles = (int32_t)n_qt;
   p.scale_log2 = softmax_scale * kLog2e;
-  hipError_t e = launch<true>(p, d, causal != 0, (uint32_t)grid, static_cast<hipStream_t>(stream));
+  p.win_left = window_side(win_left, max_seqlen, max_seqlen);
+  p.win_right = window_side(win_right, max_seqlen, max_seqlen);
+  p.band_off = 0;
+  hipError_t e = launch<true>(p, d, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                 float softmax_scale, int32_t causal, void* stream) {
+  g_last_error.clear();
+  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, softmax_scale, causal,
+                   causal == 1 ? Mask::kCausal : Mask::kNone, 0, 0, stream);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                        int32_t total, int32_t H, int32_t d, float softmax_scale,
+                        int32_t causal, void* stream) {
+  g_last_error.clear();
+  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d,
+                    softmax_scale, causal, causal == 1 ? Mask::kCausal : Mask::kNone, 0, 0,
+                    stream);
+}
+
+fa_status fa_fwd_band(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                      float softmax_scale, int32_t window_left, int32_t window_right,
+                      void* stream) {
+  g_last_error.clear();
+  const fa_status st = check_window(window_left, window_right);
+  if (st != FA_OK) return st;
+  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, softmax_scale, 0, Mask::kBand,
+                   window_left, window_right, stream);
+}
+
+fa_status fa_fwd_varlen_band(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                             int32_t total, int32_t H, int32_t d, float softmax_scale,
+                             int32_t window_left, int32_t window_right, void* stream) {
+  g_last_error.clear();
+  const fa_status st = check_window(window_left, window_right);
+  if (st != FA_OK) return st;
+  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d,
+                    softmax_scale, 0, Mask::kBand, window_left, window_right, stream);
 }
 
 const char* fa_status_string(int32_t status) {

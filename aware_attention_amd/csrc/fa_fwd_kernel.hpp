@@ -88,6 +88,11 @@ struct FwdParams {
   int32_t nbatch;              // B (dense) or num_seqs (varlen)
   int32_t n_qtiles;            // query tiles per (batch or sequence, head)
   float scale_log2;            // softmax_scale * log2(e), >= 0
+  // Band (BAND instances only): query i sees key j iff
+  // i + band_off - win_left <= j <= i + band_off + win_right.
+  int32_t win_left;            // >= 0; an unbounded side is passed as Nq + Nk + 1
+  int32_t win_right;           // >= 0; likewise
+  int32_t band_off;            // Nk - Nq (dense), 0 (varlen)
 };
 
 constexpr int kWaves = 8;                 // two groups of four
@@ -183,11 +188,17 @@ struct TileLayout {
 // where the per-lane state needs up to 256 VGPRs. At d = 32 the state fits
 // in 128 VGPRs, so two workgroups share a CU (four waves per SIMD): the
 // softmax dominates there, and the extra waves hide its latency.
-template <int D, bool CAUSAL, bool VARLEN>
+// BAND selects the banded mask (FlashAttention composes with banded masks:
+// "FlashAttention/zh", section 變體與後續版本; each token attends a local
+// window and window attention skips the key blocks outside it: "YOLOv12官版
+// 镜像集成Flash Attention v2，提速原理浅析", section 4.2). A row that sees no
+// key gets O = 0 and L = -inf.
+template <int D, bool CAUSAL, bool VARLEN, bool BAND = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D == 32 ? 4 : 2, D == 32 ? 4 : 2)))
 void fwd_kernel(FwdParams p) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
+  static_assert(!(CAUSAL && BAND), "causal is the band (unbounded, 0)");
   constexpr int BC = kBC;
   using TL = TileLayout<D>;
   constexpr int RB = TL::kRowBytes;
@@ -270,13 +281,32 @@ void fwd_kernel(FwdParams p) {
 
   const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
   const int n_kt = (kend + BC - 1) / BC;
+  // Key tiles [kt0, kt_end) hold a visible key for some row of the
+  // workgroup; with a band, keys j visible from row i satisfy
+  // i + band_lo <= j <= i + band_hi, and the range may be empty.
+  int kt0 = 0, kt_end = n_kt, band_lo = 0, band_hi = 0;
+  if constexpr (BAND) {
+    band_lo = p.band_off - p.win_left;
+    band_hi = p.band_off + p.win_right;
+    const int k_lo = max(0, q0 + band_lo);
+    const int k_hi = min(Nk - 1, min(Nq, q0 + kBR) - 1 + band_hi);
+    kt0 = k_lo / BC;
+    kt_end = k_hi >= k_lo ? k_hi / BC + 1 : kt0;
+  }
 
   // ---- Q rows of this lane, kept in VGPRs ----
   const int qw0 = q0 + wave * 32;        // first query row of this wavefront
   const int qrow = qw0 + l32;            // this lane's query row
   const bool wave_has_rows = qw0 < Nq;
-  // Last key tile that has a visible key for some row of this wavefront.
-  const int wave_last_kt = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BC) : n_kt - 1;
+  // First and last key tiles with a visible key for some row of this wavefront.
+  int wave_first_kt = 0;
+  int wave_last_kt = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BC) : n_kt - 1;
+  if constexpr (BAND) {
+    const int w_lo = max(0, qw0 + band_lo);
+    const int w_hi = min(Nk - 1, min(Nq - 1, qw0 + 31) + band_hi);
+    wave_first_kt = w_lo / BC;
+    wave_last_kt = w_hi >= w_lo ? w_hi / BC : -1;
+  }
   bf16x8 qr[DS];
   if (qrow < Nq) {
     const u32x4* src = reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * rs);
@@ -450,7 +480,8 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = key < Nk && (!CAUSAL || key <= qrow);
+          bool ok = key < Nk && (!CAUSAL || key <= qrow);
+          if constexpr (BAND) ok = ok && key >= qrow + band_lo && key <= qrow + band_hi;
           s[kb][r] = ok ? s[kb][r] * s2 : kNegInf;
           mt = fmaxf(mt, s[kb][r]);
         }
@@ -469,13 +500,17 @@ void fwd_kernel(FwdParams p) {
       // it into selects, every tile pays the multiply of the accumulator.
       asm volatile("" ::: "memory");
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // A band row that still sees no key has m_run = m_new = -inf; its
+      // state is all zeros and stays so (alpha 1 instead of exp2(NaN)).
+      const float alpha = (BAND && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
       m_run = m_new;
     }
-    const float neg_m = -m_run;
+    // A row that has seen no key yet (band only) keeps m = -inf; its
+    // exponentials are of -inf and must come out 0, not NaN.
+    const float neg_m = (BAND && m_run == kNegInf) ? 0.f : -m_run;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -504,13 +539,16 @@ void fwd_kernel(FwdParams p) {
 
   auto softmax = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
-    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0))
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0) ||
+        (BAND && (k0 < qw0 + 31 + band_lo || k0 + BC - 1 > qw0 + band_hi)))
       softmax_tile(std::true_type{}, k0);
     else
       softmax_tile(std::false_type{}, k0);
   };
 
-  auto active = [&](int kt) __attribute__((always_inline)) { return wave_has_rows && kt <= wave_last_kt; };
+  auto active = [&](int kt) __attribute__((always_inline)) {
+    return wave_has_rows && kt <= wave_last_kt && (!BAND || kt >= wave_first_kt);
+  };
 
   // ---- schedule ----
   // One workgroup barrier per key tile. In period j (between barriers j-1
@@ -524,12 +562,9 @@ void fwd_kernel(FwdParams p) {
   // period j held K_{j-1} and V_{j-2}, last read in period j-1; the copies
   // land (s_waitcnt by the issuing waves) before barrier j, ahead of their
   // first readers in period j+1.
-  if (!group_b) copy_k(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   auto mfma_phase = [&](int j) __attribute__((always_inline)) {
-    const bool do_qk = j < n_kt && active(j);
-    const bool do_pv = j >= 1 && active(j - 1);
+    const bool do_qk = j < kt_end && active(j);
+    const bool do_pv = j > kt0 && active(j - 1);
     if (do_qk && do_pv) {
       qk_pv(j, [] {});
     } else {
@@ -543,49 +578,69 @@ void fwd_kernel(FwdParams p) {
   // same in every wave, so all waves cross the same barriers.
   const int full_kt = Nk / BC;                         // tiles with BC keys
   const int unmasked_kt = CAUSAL ? min(full_kt, q0 / BC) : full_kt;
-  const int j_steady = (q0 + kBR <= Nq) ? max(1, min(unmasked_kt, full_kt - 1)) : 1;
+  // Steady periods are [js0, js1); the first tile's period and the ones
+  // after js1 take the general path.
+  int js0 = 1;
+  int js1 = (q0 + kBR <= Nq) ? max(1, min(unmasked_kt, full_kt - 1)) : 1;
+  if constexpr (BAND) {
+    // Tiles every row of the workgroup sees in full: keys from the last
+    // row's lower bound to the first row's upper bound.
+    js0 = kt0 + 1;
+    js1 = js0;
+    if (q0 + kBR <= Nq) {
+      const int t_a = (max(0, q0 + kBR - 1 + band_lo) + BC - 1) / BC;
+      const int t_b = (q0 + band_hi + 1) / BC - 1;
+      js0 = max(js0, t_a + 1);
+      js1 = max(js0, min(min(t_b, full_kt - 2), kt_end - 2) + 1);
+    }
+  }
   auto period = [&](int j) __attribute__((always_inline)) {
     if (!group_b) {
-      if (j < n_kt) {
-        if (j + 1 < n_kt) copy_k(j + 1);
+      if (j < kt_end) {
+        if (j + 1 < kt_end) copy_k(j + 1);
         copy_v(j);
       }
       mfma_phase(j);
-      if (j < n_kt && active(j)) softmax(j);
+      if (j < kt_end && active(j)) softmax(j);
       __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
     } else {
-      if (j >= 1 && active(j - 1)) softmax(j - 1);
+      if (j > kt0 && active(j - 1)) softmax(j - 1);
       mfma_phase(j);
     }
     barrier_nofence();
   };
-  period(0);
-  for (int j = 1; j < j_steady; ++j) {
-    if (!group_b) {
-      const uint8_t* gk = kg + (int64_t)((j + 1) * BC) * rs_bytes;
-      const uint8_t* gv = vg + (int64_t)(j * BC) * rs_bytes;
-      const uint32_t lk = smem_lds + ((j + 1) & 1) * TILE_BYTES + gw * NPW * 1024;
-      const uint32_t lv = smem_lds + (2 + (j & 1)) * TILE_BYTES + gw * NPW * 1024;
-      qk_pv(j, [&]() __attribute__((always_inline)) {
+  if (kt0 < kt_end) {   // a band can leave a workgroup without any key
+    if (!group_b) copy_k(kt0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int j = kt0; j < js0; ++j) period(j);
+    for (int j = js0; j < js1; ++j) {
+      if (!group_b) {
+        const uint8_t* gk = kg + (int64_t)((j + 1) * BC) * rs_bytes;
+        const uint8_t* gv = vg + (int64_t)(j * BC) * rs_bytes;
+        const uint32_t lk = smem_lds + ((j + 1) & 1) * TILE_BYTES + gw * NPW * 1024;
+        const uint32_t lv = smem_lds + (2 + (j & 1)) * TILE_BYTES + gw * NPW * 1024;
+        qk_pv(j, [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NPW; ++n) copy16_to_lds(gk, (uint32_t)k_src[n], lk + n * 1024);
+          for (int n = 0; n < NPW; ++n) copy16_to_lds(gk, (uint32_t)k_src[n], lk + n * 1024);
 #pragma unroll
-        for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
-      });
-      softmax_tile(std::false_type{}, 0);
-      __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
-    } else {
-      softmax_tile(std::false_type{}, 0);
-      qk_pv(j, [] {});
+          for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
+        });
+        softmax_tile(std::false_type{}, 0);
+        __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
+      } else {
+        softmax_tile(std::false_type{}, 0);
+        qk_pv(j, [] {});
+      }
+      barrier_nofence();
     }
-    barrier_nofence();
+    for (int j = js1; j <= kt_end; ++j) period(j);
   }
-  for (int j = j_steady; j <= n_kt; ++j) period(j);
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Nq) {
-    const float inv = __builtin_amdgcn_rcpf(l_tot);
+    const float inv = (BAND && l_tot == 0.f) ? 0.f : __builtin_amdgcn_rcpf(l_tot);
     uint16_t* orow = p.o + q_off + (int64_t)qrow * rs;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -597,7 +652,8 @@ void fwd_kernel(FwdParams p) {
         *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * hi) = w;
       }
     }
-    if (hi == 0) p.lse[l_off + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (hi == 0)
+      p.lse[l_off + qrow] = (BAND && l_tot == 0.f) ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 

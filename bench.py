@@ -11,7 +11,8 @@ synchronisations. Prints ONE JSON line.
 
 Default workload: B=1, H=32, N=8192, d=128, causal (LLM-prefill shape), the
 configuration the MFMA-utilisation target is quoted on. FLOPs per step are
-4*N*N*d*H*B halved for causal. The CPU baseline is the float64 oracle timed
+4*N*N*d*H*B halved for causal; for a banded workload, 4*d*H*B times the
+exact number of visible (query, key) pairs. The CPU baseline is the float64 oracle timed
 on the host on a bounded sample of the same workload (whole heads).
 """
 from __future__ import annotations
@@ -79,7 +80,8 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0):
         per_head = spec.flops() / (spec.B * spec.H)
         for b, h in pairs:
             f64 = lambda x: W.bf16_bits_to_f32(x[b, :, h]).astype(np.float64)  # noqa: E731
-            attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal)
+            attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal,
+                      window=spec.window)
             flops += per_head
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
@@ -147,9 +149,12 @@ def main():
         flops = spec.flops()
         config = {"workload": args.workload, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
                   "causal": spec.causal}
+        if spec.window is not None:
+            config["window"] = list(spec.window)
 
         def step():
-            aa.fa_fwd(q, k, v, softmax_scale=spec.scale, causal=spec.causal, out=o, lse=lse)
+            aa.fa_fwd(q, k, v, softmax_scale=spec.scale, causal=spec.causal, out=o, lse=lse,
+                      window=spec.window)
     else:
         cu = torch.from_numpy(wl["cu_seqlens"]).cuda()
         total = q.shape[0]

@@ -90,6 +90,42 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int32_t total, int32_t H, int32_t d, float softmax_scale,
                         int32_t causal, void* stream);
 
+/*
+ * Banded (sliding-window) mask, equal-length batch. Same tensors, layouts and
+ * requirements as fa_fwd, with the causal flag replaced by a band: query i
+ * sees key j iff
+ *     i + (Nk - Nq) - window_left <= j <= i + (Nk - Nq) + window_right,
+ * i.e. the band is centred on the query's position aligned so that the last
+ * query meets the last key (for Nq == Nk, on the diagonal). window_left and
+ * window_right are >= 0, or -1 for no bound on that side: (-1, 0) is causal
+ * attention (also for Nq != Nk, aligned as above), (-1, -1) is unmasked.
+ * Key tiles outside every row's band are neither loaded nor computed. A row
+ * that sees no key gets o = 0 and lse = -inf (the log of an empty sum).
+ *   Source: FlashAttention composes with banded masks, "FlashAttention/zh",
+ *   section 變體與後續版本; each token attends a local window and window
+ *   attention skips the key blocks outside it, "YOLOv12官版镜像集成Flash
+ *   Attention v2，提速原理浅析", section 4.2 (dynamic sparse attention).
+ * Errors: as fa_fwd; a window side below -1 is FA_ERR_INVALID_ARGUMENT;
+ * Nq or Nk above 2^29 is FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_fwd_band(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                      float softmax_scale, int32_t window_left, int32_t window_right,
+                      void* stream);
+
+/*
+ * Banded mask, packed variable-length batch. Same tensors, layouts and
+ * requirements as fa_fwd_varlen; within each sequence (queries and keys have
+ * the same length, so the alignment offset is 0) query i sees key j iff
+ * i - window_left <= j <= i + window_right, sides >= 0 or -1 as above.
+ * Errors: as fa_fwd_varlen; a window side below -1 is
+ * FA_ERR_INVALID_ARGUMENT; max_seqlen above 2^29 is FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_fwd_varlen_band(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                             int32_t total, int32_t H, int32_t d, float softmax_scale,
+                             int32_t window_left, int32_t window_right, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int32_t status);
 

@@ -138,3 +138,64 @@ def test_product_path_never_touches_the_oracle():
         if f.endswith(".py"):
             src = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
             assert "aware_attention_amd" not in src and "workloads" not in src, f
+
+
+def _band(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Nq=128, Nk=96, H=2, d=64, scale=0.125,
+             left=16, right=0, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd_band(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Nq"],
+                                a["Nk"], a["H"], a["d"], a["scale"], a["left"], a["right"],
+                                a["stream"])
+
+
+def _varlen_band(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cu=P, num_seqs=2, max_seqlen=100, total=150, H=2, d=32,
+             scale=0.1, left=-1, right=7, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd_varlen_band(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"],
+                                       a["num_seqs"], a["max_seqlen"], a["total"], a["H"], a["d"],
+                                       a["scale"], a["left"], a["right"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(left=-2), INV), (dict(right=-5), INV), (dict(q=None), INV), (dict(Nk=0), INV),
+    (dict(lse=P + 4), INV), (dict(scale=float("nan")), INV), (dict(d=96), UNS),
+    (dict(Nq=(1 << 29) + 1), UNS), (dict(Nk=(1 << 29) + 1), UNS),
+])
+def test_fa_fwd_band_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _band(**kw) == code
+    assert _lib.load().fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(left=-3), INV), (dict(cu=None), INV), (dict(max_seqlen=200, total=150), INV),
+    (dict(d=16), UNS), (dict(max_seqlen=(1 << 29) + 1, total=1 << 30), UNS),
+])
+def test_fa_fwd_varlen_band_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _varlen_band(**kw) == code
+
+
+def test_band_valid_call_without_a_device_is_a_hip_error():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    for left, right in [(-1, -1), (-1, 0), (0, 0), (2**31 - 1, 5)]:
+        assert _band(left=left, right=right) == HIP
+    assert _varlen_band() == HIP
+
+
+def test_binding_window_arguments():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        aa._window((None, 0), causal=True)
+    with pytest.raises(ValueError):
+        aa._window((-1, 0), causal=False)
+    assert aa._window((None, None), causal=False) == (-1, -1)
+    assert aa._window((3, 10**12), causal=False) == (3, 2**31 - 1)
+    with pytest.raises(ValueError):
+        aa.fa_fwd(x, x, x, window=(4, 4))   # host tensors are refused before any window use

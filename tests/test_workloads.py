@@ -66,3 +66,23 @@ def test_flop_formulas():
     assert W.WORKLOADS["prefill8k"].flops() == pytest.approx(2 * 8192**2 * 128 * 32)
     assert W.WORKLOADS["vit"].flops() == pytest.approx(4 * 1025**2 * 128 * 25 * 32)
     assert W.varlen_flops([2, 3], 4, 8, False) == 4 * 8 * 4 * 13
+
+
+def test_band_pair_count():
+    # Closed forms, then brute force over a grid of small shapes.
+    assert W.band_pairs(50, 50, (None, 0)) == 50 * 51 // 2
+    assert W.band_pairs(30, 70, (None, None)) == 30 * 70
+    assert W.band_pairs(40, 40, (0, 0)) == 40
+    N, w = 8192, 2048
+    assert W.band_pairs(N, N, (w - 1, 0)) == (w - 1) * w // 2 + (N - w + 1) * w
+    assert W.WORKLOADS["band8k"].flops() == pytest.approx(4.0 * 14681088 * 128 * 32)
+    for Nq in (1, 5, 9):
+        for Nk in (1, 4, 11):
+            for window in [(None, 0), (2, 3), (0, None), (7, 0), (0, 0), (20, 20)]:
+                left, right = window
+                n = 0
+                for i in range(Nq):
+                    for j in range(Nk):
+                        p = i + Nk - Nq
+                        n += (left is None or j >= p - left) and (right is None or j <= p + right)
+                assert W.band_pairs(Nq, Nk, window) == n, (Nq, Nk, window)

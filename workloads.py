@@ -12,6 +12,8 @@ Workloads (shapes follow the pages' models):
   varlen      64 sequences, lengths ~U{256..1025}, H=25 d=128, non-causal  seed 4
   prefill8k   B=1  H=32 N=8192 d=128  causal                 seed 5
   prefill2k   B=4  H=32 N=2048 d=128  causal                 seed 55
+  band8k      B=1  H=32 N=8192 d=128  band (2047, 0): each query sees itself
+              and the 2047 keys before it                    seed 6
 
 The detector token counts (40x40, 20x20 and the 4-head, 32-wide head split)
 come from "YOLOv12官版镜像集成Flash Attention v2，提速原理浅析" (sections 2.1 and
@@ -81,12 +83,17 @@ class Dense:
     causal: bool
     seed: int
     rms_qk: bool = False
+    window: tuple | None = None   # banded mask (left, right), None = unbounded side
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     def flops(self) -> float:
+        """Useful FLOPs: 4 d per (query, visible key) pair, the causal count
+        taken as N^2 / 2, the band's as its exact pair count."""
+        if self.window is not None:
+            return 4.0 * band_pairs(self.N, self.N, self.window) * self.d * self.H * self.B
         f = 4.0 * self.N * self.N * self.d * self.H * self.B
         return f / 2 if self.causal else f
 
@@ -121,7 +128,20 @@ WORKLOADS = {
                      causal=False, seed=4),
     "prefill8k": Dense("prefill8k", B=1, H=32, N=8192, d=128, causal=True, seed=5),
     "prefill2k": Dense("prefill2k", B=4, H=32, N=2048, d=128, causal=True, seed=55),
+    "band8k": Dense("band8k", B=1, H=32, N=8192, d=128, causal=False, seed=6,
+                    window=(2047, 0)),
 }
+
+
+def band_pairs(Nq: int, Nk: int, window) -> int:
+    """Number of (query, key) pairs a banded mask leaves visible, for FLOP
+    accounting: row i sees keys max(0, i + Nk - Nq - left) ..
+    min(Nk - 1, i + Nk - Nq + right), None meaning no bound on that side."""
+    left, right = window
+    i = np.arange(Nq, dtype=np.int64) + (Nk - Nq)
+    lo = np.zeros_like(i) if left is None else np.maximum(0, i - left)
+    hi = np.full_like(i, Nk - 1) if right is None else np.minimum(Nk - 1, i + right)
+    return int(np.maximum(0, hi - lo + 1).sum())
 
 
 def _draw(rng: np.random.Generator, shape) -> np.ndarray:
