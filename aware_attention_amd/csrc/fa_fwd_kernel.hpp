@@ -53,7 +53,8 @@
 // keys past the sequence end and, when causal, keys after the query are set
 // to -inf, only on the tiles that need it; tiles entirely above a wavefront's
 // diagonal are skipped, and key tiles past the workgroup's last query are
-// never loaded.
+// never loaded. A banded mask (same section: the fused kernel composes with
+// banded masks) likewise loads only the key tiles inside some row's band.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,8 +91,8 @@ struct FwdParams {
   float scale_log2;            // softmax_scale * log2(e), >= 0
   // Band (BAND instances only): query i sees key j iff
   // i + band_off - win_left <= j <= i + band_off + win_right.
-  int32_t win_left;            // >= 0; an unbounded side is passed as Nq + Nk + 1
-  int32_t win_right;           // >= 0; likewise
+  int32_t win_left;            // >= 0; an unbounded side is passed as max(Nq, Nk)
+  int32_t win_right;           // >= 0; likewise (varlen: max_seqlen)
   int32_t band_off;            // Nk - Nq (dense), 0 (varlen)
 };
 
@@ -193,6 +194,24 @@ struct TileLayout {
 // window and window attention skips the key blocks outside it: "YOLOv12官版
 // 镜像集成Flash Attention v2，提速原理浅析", section 4.2). A row that sees no
 // key gets O = 0 and L = -inf.
+// Dispatch rank r (0 = first) -> query tile for a band, longest rows first.
+// Tile t (q0 = t kBR) holds min(Nk, q0 + kBR + band_hi) - max(0, q0 + band_lo)
+// key columns: a concave function of q0 with slopes +1 and -1, largest
+// around q0 = c = (Nk - kBR - band_hi - band_lo) / 2. Tiles are taken by
+// distance from c, alternating sides (tile floor(c / kBR), the one after
+// it, the one before, ...), then the longer side's remainder; a causal-like
+// band (left side unbounded) gives the descending order of causal
+// attention. Returns a permutation of [0, n) over r in [0, n).
+__device__ inline int band_tile_of_rank(int r, int n, int Nk, int band_lo, int band_hi) {
+  const int64_t c2 = (int64_t)Nk - kBR - band_hi - band_lo;     // 2c
+  const int tc = c2 < 0 ? 0 : (int)min<int64_t>(c2 / (2 * kBR), n - 1);
+  const int left = tc + 1, right = n - 1 - tc;                  // tiles on each side
+  const int m = min(left, right);
+  if (r < 2 * m) return (r & 1) ? tc + 1 + (r >> 1) : tc - (r >> 1);
+  const int rest = r - 2 * m;
+  return left > right ? tc - m - rest : tc + 1 + m + rest;
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool BAND = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D == 32 ? 4 : 2, D == 32 ? 4 : 2)))
@@ -233,14 +252,15 @@ void fwd_kernel(FwdParams p) {
   //    m % n_qtiles, so an XCD works through the query tiles of a few units
   //    at a time and they share K/V tiles in its L2 (ViT-shaped batch: HBM
   //    reads 2.3 GB -> 0.64 GB per launch, +15 %).
-  //  * Otherwise, and always for causal attention, tile-major: blockIdx.x =
-  //    rank * units + unit. With a unit count that is a multiple of 8 each
-  //    XCD still sees only units congruent to its index; causal ranks run
-  //    longest rows of the mask first, across all units, which balances the
-  //    CUs (unit-grouped causal order measured 2-12 % slower).
+  //  * Otherwise, and always for causal and banded attention, tile-major:
+  //    blockIdx.x = rank * units + unit. With a unit count that is a
+  //    multiple of 8 each XCD still sees only units congruent to its index;
+  //    causal and banded ranks run the query tiles with the most key tiles
+  //    first, across all units, which balances the CUs (unit-grouped causal
+  //    order measured 2-12 % slower).
   const int per_qt = p.H * p.nbatch;   // units
   int qt, rem;
-  if (!CAUSAL && (per_qt & 7) == 0) {
+  if (!CAUSAL && !BAND && (per_qt & 7) == 0) {
     const int m = blockIdx.x >> 3;
     qt = m % p.n_qtiles;
     rem = (blockIdx.x & 7) + 8 * (m / p.n_qtiles);
@@ -269,6 +289,13 @@ void fwd_kernel(FwdParams p) {
     k_off = (int64_t)bidx * p.k_batch_stride + (int64_t)head * D;
     l_off = (int64_t)bidx * p.lse_batch_stride + (int64_t)head * p.lse_head_stride;
   }
+  int band_lo = 0, band_hi = 0;
+  if constexpr (BAND) {
+    band_lo = p.band_off - p.win_left;
+    band_hi = p.band_off + p.win_right;
+    const int n_seq = (Nq + kBR - 1) / kBR;   // this sequence's query tiles
+    if (qt < n_seq) qt = band_tile_of_rank(qt, n_seq, Nk, band_lo, band_hi);
+  }
   const int q0 = qt * kBR;
   if (q0 >= Nq) return;   // whole workgroup: tile past this sequence's end
 
@@ -284,10 +311,8 @@ void fwd_kernel(FwdParams p) {
   // Key tiles [kt0, kt_end) hold a visible key for some row of the
   // workgroup; with a band, keys j visible from row i satisfy
   // i + band_lo <= j <= i + band_hi, and the range may be empty.
-  int kt0 = 0, kt_end = n_kt, band_lo = 0, band_hi = 0;
+  int kt0 = 0, kt_end = n_kt;
   if constexpr (BAND) {
-    band_lo = p.band_off - p.win_left;
-    band_hi = p.band_off + p.win_right;
     const int k_lo = max(0, q0 + band_lo);
     const int k_hi = min(Nk - 1, min(Nq, q0 + kBR) - 1 + band_hi);
     kt0 = k_lo / BC;

@@ -91,9 +91,12 @@ def test_band_single_rows_and_keys():
 
 
 @pytest.mark.parametrize("d", [32, 128])
-def test_band_unit_grouped_order(d):
-    # 2 batches x 4 heads = 8 units: the kernel numbers query tiles unit by unit.
-    check_band(2, 600, 600, 4, d, (64, 64), seed=6200 + d)
+@pytest.mark.parametrize("window", [(64, 64), (None, 0), (0, None)])
+def test_band_tile_order(d, window):
+    # 2 batches x 4 heads = 8 units, 12 query tiles each: banded launches
+    # dispatch the query tiles with the most key tiles first (middle-out for
+    # a two-sided band, descending / ascending for one-sided ones).
+    check_band(2, 3000, 3000, 4, d, window, seed=6200 + d)
 
 
 def test_band_zero_query_closed_form():
