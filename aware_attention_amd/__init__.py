@@ -15,6 +15,11 @@ library is missing or the device is not a gfx950, calls raise.
     sees key j iff i + (Nk - Nq) - left <= j <= i + (Nk - Nq) + right (varlen:
     offset 0), None meaning no bound on that side; rows that see no key get
     o = 0 and lse = -inf (entry points fa_fwd_band / fa_fwd_varlen_band).
+    q, k, v (and out) may be float16 instead of bfloat16 (all the same type),
+    and may be strided views whose last dimension is contiguous and whose other
+    strides are multiples of 8 elements, such as q = qkv[:, :, 0] of a packed
+    (B, S, 3, H, d) tensor; such calls go through fa_fwd_strided /
+    fa_fwd_varlen_strided with no copy.
 
 The default scale is 1/sqrt(d), as in the definition on "FlashAttention/zh"
 (marovi.ai wiki), section 為何標準注意力運行緩慢. Only half precision on the
@@ -26,9 +31,10 @@ from __future__ import annotations
 
 import math
 
-from ._lib import (FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_OK, FaError,
-                   check, load, raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_varlen,
-                   raw_fa_fwd_varlen_band)
+from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
+                   FA_ERR_UNSUPPORTED, FA_OK, FaError, check, load, raw_fa_fwd, raw_fa_fwd_band,
+                   raw_fa_fwd_strided, raw_fa_fwd_varlen, raw_fa_fwd_varlen_band,
+                   raw_fa_fwd_varlen_strided)
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "FaError", "load", "FA_OK", "FA_ERR_INVALID_ARGUMENT",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
@@ -39,18 +45,48 @@ def _torch():
     return torch
 
 
+def _dtype_code(dtype):
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if dtype == torch.float16:
+        return FA_DTYPE_F16
+    raise TypeError(f"q, k, v must be bfloat16 or float16 (got {dtype})")
+
+
 def _check_tensor(t, name, ndim):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+    _dtype_code(t.dtype)
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device (got {t.device})")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last (head) dimension")
+
+
+def _strides(t):
+    """Element strides of every dimension but the last; 0 for dimensions of size 1,
+    whose stride never matters."""
+    return [t.stride(i) if t.shape[i] > 1 else 0 for i in range(t.dim() - 1)]
+
+
+def _plain(*ts):
+    """True when every tensor is contiguous bfloat16 (the entry points without strides)."""
+    torch = _torch()
+    return all(t.is_contiguous() and t.dtype == torch.bfloat16 for t in ts)
+
+
+def _out(out, like, shape, name):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=like.dtype, device=like.device)
+    _check_tensor(out, name, len(shape))
+    if tuple(out.shape) != tuple(shape) or out.dtype != like.dtype:
+        raise ValueError(f"{name} must have shape {tuple(shape)} and dtype {like.dtype}")
+    return out
 
 
 def _scale(softmax_scale, d):
@@ -76,28 +112,29 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, window
     B, Nq, H, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != d:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError(f"q, k and v must share one dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k and v must be on the same device")
     Nk = k.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, q, (B, Nq, H, d), "out")
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, Nq)")
+    scale = _scale(softmax_scale, d)
+    wl, wr = (-1, -1) if window is None else _window(window, causal)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if window is None:
-            check(raw_fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr(), B, Nq, Nk, H, d, _scale(softmax_scale, d),
-                             int(bool(causal)), stream))
+        if not _plain(q, k, v, out):
+            check(raw_fa_fwd_strided(*ptrs, B, Nq, Nk, H, d, _strides(q), _strides(k),
+                                     _strides(v), _strides(out), _dtype_code(q.dtype), scale,
+                                     int(bool(causal)), wl, wr, stream))
+        elif window is None:
+            check(raw_fa_fwd(*ptrs, B, Nq, Nk, H, d, scale, int(bool(causal)), stream))
         else:
-            wl, wr = _window(window, causal)
-            check(raw_fa_fwd_band(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  lse.data_ptr(), B, Nq, Nk, H, d, _scale(softmax_scale, d),
-                                  wl, wr, stream))
+            check(raw_fa_fwd_band(*ptrs, B, Nq, Nk, H, d, scale, wl, wr, stream))
     return out, lse
 
 
@@ -110,29 +147,32 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=Fa
     total, H, d = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k and v must share the packed shape (total, H, d)")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError(f"q, k and v must share one dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
             or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
     num_seqs = cu_seqlens.numel() - 1
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, q, (total, H, d), "out")
     if lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape (H, total)")
+    scale = _scale(softmax_scale, d)
+    wl, wr = (-1, -1) if window is None else _window(window, causal)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            cu_seqlens.data_ptr())
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if window is None:
-            check(raw_fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                    lse.data_ptr(), cu_seqlens.data_ptr(), num_seqs,
-                                    int(max_seqlen), total, H, d, _scale(softmax_scale, d),
+        if not _plain(q, k, v, out):
+            check(raw_fa_fwd_varlen_strided(*ptrs, num_seqs, int(max_seqlen), total, H, d,
+                                            _strides(q), _strides(k), _strides(v),
+                                            _strides(out), _dtype_code(q.dtype), scale,
+                                            int(bool(causal)), wl, wr, stream))
+        elif window is None:
+            check(raw_fa_fwd_varlen(*ptrs, num_seqs, int(max_seqlen), total, H, d, scale,
                                     int(bool(causal)), stream))
         else:
-            wl, wr = _window(window, causal)
-            check(raw_fa_fwd_varlen_band(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                         out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(),
-                                         num_seqs, int(max_seqlen), total, H, d,
-                                         _scale(softmax_scale, d), wl, wr, stream))
+            check(raw_fa_fwd_varlen_band(*ptrs, num_seqs, int(max_seqlen), total, H, d, scale,
+                                         wl, wr, stream))
     return out, lse

@@ -14,8 +14,11 @@ FA_ERR_INVALID_ARGUMENT = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_status_string",
-            "fa_last_error", "fa_abi_version")
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F16 = 1
+
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
+            "fa_fwd_varlen_strided", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -47,6 +50,13 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen_band.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                        i32, vp]
     lib.fa_fwd_varlen_band.restype = i32
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, p64, p64, p64, p64,
+                                   i32, f32, i32, i32, i32, vp]
+    lib.fa_fwd_strided.restype = i32
+    lib.fa_fwd_varlen_strided.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, p64, p64,
+                                          p64, p64, i32, f32, i32, i32, i32, vp]
+    lib.fa_fwd_varlen_strided.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -89,3 +99,27 @@ def raw_fa_fwd_varlen_band(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, 
     """Pointer-level call of fa_fwd_varlen_band; returns the status code."""
     return load().fa_fwd_varlen_band(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d,
                                      scale, window_left, window_right, stream)
+
+
+def _int64_array(x):
+    """A host int64 array holding the sequence x (None passes a null pointer)."""
+    return None if x is None else (ctypes.c_int64 * len(x))(*[int(e) for e in x])
+
+
+def raw_fa_fwd_strided(q, k, v, o, lse, B, Nq, Nk, H, d, q_strides, k_strides, v_strides,
+                       o_strides, dtype, scale, causal, window_left, window_right, stream) -> int:
+    """Pointer-level call of fa_fwd_strided (strides: sequences of 3 ints); returns the status."""
+    return load().fa_fwd_strided(q, k, v, o, lse, B, Nq, Nk, H, d, _int64_array(q_strides),
+                                 _int64_array(k_strides), _int64_array(v_strides),
+                                 _int64_array(o_strides), dtype, scale, causal, window_left,
+                                 window_right, stream)
+
+
+def raw_fa_fwd_varlen_strided(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d, q_strides,
+                              k_strides, v_strides, o_strides, dtype, scale, causal, window_left,
+                              window_right, stream) -> int:
+    """Pointer-level call of fa_fwd_varlen_strided (strides: sequences of 2 ints)."""
+    return load().fa_fwd_varlen_strided(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d,
+                                        _int64_array(q_strides), _int64_array(k_strides),
+                                        _int64_array(v_strides), _int64_array(o_strides), dtype,
+                                        scale, causal, window_left, window_right, stream)

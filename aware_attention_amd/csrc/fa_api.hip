@@ -53,32 +53,39 @@ fa_status check_device() {
   return FA_OK;
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool BAND>
+template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16>
 hipError_t launch_one(const fa::FwdParams& p, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN, BAND>), dim3(grid), dim3(fa::kThreads),
-                     0, stream, p);
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN, BAND, F16>), dim3(grid),
+                     dim3(fa::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 // Mask of a launch: none, causal (top-left, Nq == Nk) or a band.
 enum class Mask { kNone, kCausal, kBand };
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool F16>
 hipError_t launch_d(const fa::FwdParams& p, Mask mask, uint32_t grid, hipStream_t stream) {
   switch (mask) {
-    case Mask::kCausal: return launch_one<D, true, VARLEN, false>(p, grid, stream);
-    case Mask::kBand: return launch_one<D, false, VARLEN, true>(p, grid, stream);
-    default: return launch_one<D, false, VARLEN, false>(p, grid, stream);
+    case Mask::kCausal: return launch_one<D, true, VARLEN, false, F16>(p, grid, stream);
+    case Mask::kBand: return launch_one<D, false, VARLEN, true, F16>(p, grid, stream);
+    default: return launch_one<D, false, VARLEN, false, F16>(p, grid, stream);
+  }
+}
+
+template <bool VARLEN, bool F16>
+hipError_t launch_t(const fa::FwdParams& p, int d, Mask mask, uint32_t grid, hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_d<32, VARLEN, F16>(p, mask, grid, stream);
+    case 64: return launch_d<64, VARLEN, F16>(p, mask, grid, stream);
+    default: return launch_d<128, VARLEN, F16>(p, mask, grid, stream);
   }
 }
 
 template <bool VARLEN>
-hipError_t launch(const fa::FwdParams& p, int d, Mask mask, uint32_t grid, hipStream_t stream) {
-  switch (d) {
-    case 32: return launch_d<32, VARLEN>(p, mask, grid, stream);
-    case 64: return launch_d<64, VARLEN>(p, mask, grid, stream);
-    default: return launch_d<128, VARLEN>(p, mask, grid, stream);
-  }
+hipError_t launch(const fa::FwdParams& p, int d, int32_t dtype, Mask mask, uint32_t grid,
+                  hipStream_t stream) {
+  return dtype == FA_DTYPE_F16 ? launch_t<VARLEN, true>(p, d, mask, grid, stream)
+                               : launch_t<VARLEN, false>(p, d, mask, grid, stream);
 }
 
 // Window sides: >= 0, or -1 for unbounded. A side of max(nq, nk) already
@@ -97,27 +104,80 @@ int32_t window_side(int32_t w, int64_t nq, int64_t nk) {
   return (int32_t)((w < 0 || w > unbounded) ? unbounded : w);
 }
 
-fa_status check_common(int32_t H, int32_t d, float scale, int32_t causal) {
-  if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
+// The mask named by a causal flag and a window, as taken by the strided
+// entry points: causal, or no mask when both sides are unbounded, else a band.
+fa_status mask_of(int32_t causal, int32_t left, int32_t right, Mask* mask) {
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  const fa_status st = check_window(left, right);
+  if (st != FA_OK) return st;
+  const bool unbounded = left == -1 && right == -1;
+  if (causal && !unbounded)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal and a window are exclusive (causal is window (-1, 0))");
+  *mask = causal ? Mask::kCausal : (unbounded ? Mask::kNone : Mask::kBand);
+  return FA_OK;
+}
+
+// Strides of one tensor in elements (d contiguous): batch (dense only),
+// token, head.
+struct Strides {
+  int64_t b, t, h;
+};
+// Token strides up to 2^24 elements keep the kernel's per-lane 32-bit byte
+// offsets inside a 64-row tile in range.
+constexpr int64_t kMaxTokenStride = int64_t{1} << 24;
+
+fa_status check_strides(const Strides& s, const char* name) {
+  if (s.b < 0 || s.t < 0 || s.h < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, std::string(name) + ": strides must be >= 0");
+  if ((s.b | s.t | s.h) & 7)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                std::string(name) + ": strides must be multiples of 8 elements (16-byte aligned rows)");
+  if (s.t > kMaxTokenStride)
+    return fail(FA_ERR_UNSUPPORTED, std::string(name) + ": token stride above 2^24 elements");
+  return FA_OK;
+}
+
+fa_status check_dtype(int32_t dtype) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+    return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
+  return FA_OK;
+}
+
+fa_status check_common(int32_t H, int32_t d, float scale) {
+  if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
   if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
   return FA_OK;
 }
 
-constexpr float kLog2e = 1.44269504088896340736f;
+void set_strides(fa::FwdParams& p, const Strides st[4]) {
+  p.q_bs = st[0].b; p.q_ts = st[0].t; p.q_hs = st[0].h;
+  p.k_bs = st[1].b; p.k_ts = st[1].t; p.k_hs = st[1].h;
+  p.v_bs = st[2].b; p.v_ts = st[2].t; p.v_hs = st[2].h;
+  p.o_bs = st[3].b; p.o_ts = st[3].t; p.o_hs = st[3].h;
+}
 
-// Equal-length batch; the arguments other than the mask are those of fa_fwd.
+constexpr float kLog2e = 1.44269504088896340736f;
+const char* const kTensorNames[4] = {"q", "k", "v", "o"};
+
+// Equal-length batch, any strides, either element type, any mask.
 fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                     int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
-                    float softmax_scale, int32_t causal, Mask mask, int32_t win_left,
-                    int32_t win_right, void* stream) {
+                    const Strides st[4], int32_t dtype, float softmax_scale, Mask mask,
+                    int32_t win_left, int32_t win_right, void* stream) {
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (B < 1 || Nq < 1 || Nk < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B, Nq and Nk must be >= 1");
-  fa_status st = check_common(H, d, softmax_scale, causal);
-  if (st != FA_OK) return st;
-  if (causal && Nq != Nk) return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
+  fa_status st_ = check_common(H, d, softmax_scale);
+  if (st_ != FA_OK) return st_;
+  st_ = check_dtype(dtype);
+  if (st_ != FA_OK) return st_;
+  for (int i = 0; i < 4; ++i) {
+    st_ = check_strides(st[i], kTensorNames[i]);
+    if (st_ != FA_OK) return st_;
+  }
+  if (mask == Mask::kCausal && Nq != Nk)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
   if (mask == Mask::kBand && (Nq > kMaxBandLen || Nk > kMaxBandLen))
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -125,8 +185,8 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   const int64_t n_qt = (Nq + fa::kBR - 1) / fa::kBR;
   const int64_t grid = n_qt * H * (int64_t)B;
   if (grid > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many query tiles for one launch");
-  st = check_device();
-  if (st != FA_OK) return st;
+  st_ = check_device();
+  if (st_ != FA_OK) return st_;
 
   fa::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -135,9 +195,7 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.cu_seqlens = nullptr;
-  p.row_stride = (int64_t)H * d;
-  p.q_batch_stride = (int64_t)Nq * H * d;
-  p.k_batch_stride = (int64_t)Nk * H * d;
+  set_strides(p, st);
   p.lse_head_stride = Nq;
   p.lse_batch_stride = (int64_t)H * Nq;
   p.Nq = Nq;
@@ -149,24 +207,30 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   p.win_left = window_side(win_left, Nq, Nk);
   p.win_right = window_side(win_right, Nq, Nk);
   p.band_off = Nk - Nq;
-  hipError_t e = launch<false>(p, d, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
+  hipError_t e = launch<false>(p, d, dtype, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
 }
 
-// Packed variable-length batch; the arguments other than the mask are those
-// of fa_fwd_varlen.
+// Packed variable-length batch, any token and head strides, either element
+// type, any mask (batch strides unused).
 fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
-                     int32_t total, int32_t H, int32_t d, float softmax_scale,
-                     int32_t causal, Mask mask, int32_t win_left, int32_t win_right,
+                     int32_t total, int32_t H, int32_t d, const Strides st[4], int32_t dtype,
+                     float softmax_scale, Mask mask, int32_t win_left, int32_t win_right,
                      void* stream) {
   if (!cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
   if (num_seqs < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
   if (total < 0 || max_seqlen < 0) return fail(FA_ERR_INVALID_ARGUMENT, "total and max_seqlen must be >= 0");
   if (max_seqlen > total) return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen exceeds total");
-  fa_status st = check_common(H, d, softmax_scale, causal);
-  if (st != FA_OK) return st;
+  fa_status st_ = check_common(H, d, softmax_scale);
+  if (st_ != FA_OK) return st_;
+  st_ = check_dtype(dtype);
+  if (st_ != FA_OK) return st_;
+  for (int i = 0; i < 4; ++i) {
+    st_ = check_strides(st[i], kTensorNames[i]);
+    if (st_ != FA_OK) return st_;
+  }
   if (mask == Mask::kBand && max_seqlen > kMaxBandLen)
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports max_seqlen <= 2^29");
   if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
@@ -177,8 +241,8 @@ fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float
   const int64_t n_qt = (max_seqlen + fa::kBR - 1) / fa::kBR;
   const int64_t grid = n_qt * H * (int64_t)num_seqs;
   if (grid > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many query tiles for one launch");
-  st = check_device();
-  if (st != FA_OK) return st;
+  st_ = check_device();
+  if (st_ != FA_OK) return st_;
 
   fa::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -187,9 +251,7 @@ fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.cu_seqlens = cu_seqlens;
-  p.row_stride = (int64_t)H * d;
-  p.q_batch_stride = 0;
-  p.k_batch_stride = 0;
+  set_strides(p, st);
   p.lse_head_stride = total;
   p.lse_batch_stride = 0;
   p.Nq = 0;
@@ -201,8 +263,26 @@ fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float
   p.win_left = window_side(win_left, max_seqlen, max_seqlen);
   p.win_right = window_side(win_right, max_seqlen, max_seqlen);
   p.band_off = 0;
-  hipError_t e = launch<true>(p, d, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
+  hipError_t e = launch<true>(p, d, dtype, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+// Densely packed (B, N, H, d) tensors, or (total, H, d) with batch stride 0.
+void contiguous(int64_t Nq, int64_t Nk, int32_t H, int32_t d, Strides st[4]) {
+  const int64_t t = (int64_t)H * d;
+  st[0] = {Nq * t, t, d};
+  st[1] = {Nk * t, t, d};
+  st[2] = {Nk * t, t, d};
+  st[3] = {Nq * t, t, d};
+}
+
+// Strides from the caller's arrays: n entries each (3 dense, 2 varlen).
+fa_status read_strides(const int64_t* const in[4], int n, Strides st[4]) {
+  for (int i = 0; i < 4; ++i) {
+    if (!in[i]) return fail(FA_ERR_INVALID_ARGUMENT, std::string("null stride array for ") + kTensorNames[i]);
+    st[i] = n == 3 ? Strides{in[i][0], in[i][1], in[i][2]} : Strides{0, in[i][0], in[i][1]};
+  }
   return FA_OK;
 }
 
@@ -214,8 +294,13 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
                  float softmax_scale, int32_t causal, void* stream) {
   g_last_error.clear();
-  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, softmax_scale, causal,
-                   causal == 1 ? Mask::kCausal : Mask::kNone, 0, 0, stream);
+  Mask mask;
+  const fa_status st_ = mask_of(causal, -1, -1, &mask);
+  if (st_ != FA_OK) return st_;
+  Strides st[4];
+  contiguous(Nq, Nk, H, d, st);
+  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, st, FA_DTYPE_BF16, softmax_scale, mask,
+                   -1, -1, stream);
 }
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -223,9 +308,13 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int32_t total, int32_t H, int32_t d, float softmax_scale,
                         int32_t causal, void* stream) {
   g_last_error.clear();
-  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d,
-                    softmax_scale, causal, causal == 1 ? Mask::kCausal : Mask::kNone, 0, 0,
-                    stream);
+  Mask mask;
+  const fa_status st_ = mask_of(causal, -1, -1, &mask);
+  if (st_ != FA_OK) return st_;
+  Strides st[4];
+  contiguous(0, 0, H, d, st);
+  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d, st,
+                    FA_DTYPE_BF16, softmax_scale, mask, -1, -1, stream);
 }
 
 fa_status fa_fwd_band(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -233,10 +322,12 @@ fa_status fa_fwd_band(const void* q, const void* k, const void* v, void* o, floa
                       float softmax_scale, int32_t window_left, int32_t window_right,
                       void* stream) {
   g_last_error.clear();
-  const fa_status st = check_window(window_left, window_right);
-  if (st != FA_OK) return st;
-  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, softmax_scale, 0, Mask::kBand,
-                   window_left, window_right, stream);
+  const fa_status st_ = check_window(window_left, window_right);
+  if (st_ != FA_OK) return st_;
+  Strides st[4];
+  contiguous(Nq, Nk, H, d, st);
+  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, st, FA_DTYPE_BF16, softmax_scale,
+                   Mask::kBand, window_left, window_right, stream);
 }
 
 fa_status fa_fwd_varlen_band(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -244,10 +335,49 @@ fa_status fa_fwd_varlen_band(const void* q, const void* k, const void* v, void* 
                              int32_t total, int32_t H, int32_t d, float softmax_scale,
                              int32_t window_left, int32_t window_right, void* stream) {
   g_last_error.clear();
-  const fa_status st = check_window(window_left, window_right);
-  if (st != FA_OK) return st;
-  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d,
-                    softmax_scale, 0, Mask::kBand, window_left, window_right, stream);
+  const fa_status st_ = check_window(window_left, window_right);
+  if (st_ != FA_OK) return st_;
+  Strides st[4];
+  contiguous(0, 0, H, d, st);
+  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d, st,
+                    FA_DTYPE_BF16, softmax_scale, Mask::kBand, window_left, window_right, stream);
+}
+
+fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                         const int64_t* q_strides, const int64_t* k_strides,
+                         const int64_t* v_strides, const int64_t* o_strides, int32_t dtype,
+                         float softmax_scale, int32_t causal, int32_t window_left,
+                         int32_t window_right, void* stream) {
+  g_last_error.clear();
+  Mask mask;
+  fa_status st_ = mask_of(causal, window_left, window_right, &mask);
+  if (st_ != FA_OK) return st_;
+  const int64_t* const in[4] = {q_strides, k_strides, v_strides, o_strides};
+  Strides st[4];
+  st_ = read_strides(in, 3, st);
+  if (st_ != FA_OK) return st_;
+  return dense_fwd(q, k, v, o, lse, B, Nq, Nk, H, d, st, dtype, softmax_scale, mask,
+                   window_left, window_right, stream);
+}
+
+fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                                int32_t total, int32_t H, int32_t d, const int64_t* q_strides,
+                                const int64_t* k_strides, const int64_t* v_strides,
+                                const int64_t* o_strides, int32_t dtype, float softmax_scale,
+                                int32_t causal, int32_t window_left, int32_t window_right,
+                                void* stream) {
+  g_last_error.clear();
+  Mask mask;
+  fa_status st_ = mask_of(causal, window_left, window_right, &mask);
+  if (st_ != FA_OK) return st_;
+  const int64_t* const in[4] = {q_strides, k_strides, v_strides, o_strides};
+  Strides st[4];
+  st_ = read_strides(in, 2, st);
+  if (st_ != FA_OK) return st_;
+  return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d, st, dtype,
+                    softmax_scale, mask, window_left, window_right, stream);
 }
 
 const char* fa_status_string(int32_t status) {

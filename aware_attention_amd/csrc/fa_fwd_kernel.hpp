@@ -64,9 +64,12 @@
 
 namespace fa {
 
+// Operand registers are typed bf16x8 whatever the element type; for fp16
+// inputs the same bits hold fp16 values and are reinterpreted at the MFMA.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -78,9 +81,13 @@ struct FwdParams {
   uint16_t* o;
   float* lse;
   const int32_t* cu_seqlens;   // varlen only
-  int64_t q_batch_stride;      // elements between batches of q and o (dense)
-  int64_t k_batch_stride;      // elements between batches of k and v (dense)
-  int64_t row_stride;          // elements between consecutive tokens: H * d
+  // Strides in elements of q, k, v and o (d is contiguous): between batches
+  // (dense only), consecutive tokens and heads. Token strides are at most
+  // 2^24 and every stride is a multiple of 8 (16-byte aligned rows).
+  int64_t q_bs, q_ts, q_hs;
+  int64_t k_bs, k_ts, k_hs;
+  int64_t v_bs, v_ts, v_hs;
+  int64_t o_bs, o_ts, o_hs;
   int64_t lse_batch_stride;    // dense: H * Nq
   int64_t lse_head_stride;     // dense: Nq; varlen: total
   int32_t Nq;                  // dense only
@@ -131,9 +138,27 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
+// Two floats rounded (to nearest even) to the 16-bit element type, packed
+// low then high: one v_cvt_pk_bf16_f32 or v_cvt_pk_f16_f32.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (F16) {
+    const f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// D += A B on the 32x32x16 matrix core in the element type (fp32 accumulate).
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Workgroup barrier without a memory fence: LDS operand reads of the current
@@ -212,7 +237,7 @@ __device__ inline int band_tile_of_rank(int r, int n, int Nk, int band_lo, int b
   return left > right ? tc - m - rest : tc + 1 + m + rest;
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool BAND = false>
+template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D == 32 ? 4 : 2, D == 32 ? 4 : 2)))
 void fwd_kernel(FwdParams p) {
@@ -273,20 +298,24 @@ void fwd_kernel(FwdParams p) {
   const int bidx = rem / p.H;
 
   int Nq, Nk;
-  int64_t q_off, k_off, l_off;
+  int64_t q_off, k_off, v_off, o_off, l_off;
   if (VARLEN) {
     const int start = p.cu_seqlens[bidx];
     const int len = p.cu_seqlens[bidx + 1] - start;
     Nq = len;
     Nk = len;
-    q_off = (int64_t)start * p.row_stride + (int64_t)head * D;
-    k_off = q_off;
+    q_off = (int64_t)start * p.q_ts + (int64_t)head * p.q_hs;
+    k_off = (int64_t)start * p.k_ts + (int64_t)head * p.k_hs;
+    v_off = (int64_t)start * p.v_ts + (int64_t)head * p.v_hs;
+    o_off = (int64_t)start * p.o_ts + (int64_t)head * p.o_hs;
     l_off = (int64_t)head * p.lse_head_stride + start;
   } else {
     Nq = p.Nq;
     Nk = p.Nk;
-    q_off = (int64_t)bidx * p.q_batch_stride + (int64_t)head * D;
-    k_off = (int64_t)bidx * p.k_batch_stride + (int64_t)head * D;
+    q_off = (int64_t)bidx * p.q_bs + (int64_t)head * p.q_hs;
+    k_off = (int64_t)bidx * p.k_bs + (int64_t)head * p.k_hs;
+    v_off = (int64_t)bidx * p.v_bs + (int64_t)head * p.v_hs;
+    o_off = (int64_t)bidx * p.o_bs + (int64_t)head * p.o_hs;
     l_off = (int64_t)bidx * p.lse_batch_stride + (int64_t)head * p.lse_head_stride;
   }
   int band_lo = 0, band_hi = 0;
@@ -301,9 +330,11 @@ void fwd_kernel(FwdParams p) {
 
   const uint16_t* __restrict__ qg = p.q + q_off;
   const uint8_t* __restrict__ kg = reinterpret_cast<const uint8_t*>(p.k + k_off);
-  const uint8_t* __restrict__ vg = reinterpret_cast<const uint8_t*>(p.v + k_off);
-  const int rs = (int)p.row_stride;          // elements
-  const int rs_bytes = 2 * rs;
+  const uint8_t* __restrict__ vg = reinterpret_cast<const uint8_t*>(p.v + v_off);
+  const int q_ts = (int)p.q_ts;              // token strides: elements
+  const int o_ts = (int)p.o_ts;
+  const int k_tb = 2 * (int)p.k_ts;          // ... and bytes
+  const int v_tb = 2 * (int)p.v_ts;
   const float s2 = p.scale_log2;
 
   const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
@@ -334,7 +365,7 @@ void fwd_kernel(FwdParams p) {
   }
   bf16x8 qr[DS];
   if (qrow < Nq) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * rs);
+    const u32x4* src = reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * q_ts);
 #pragma unroll
     for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, src[2 * s + hi]);
   } else {
@@ -352,12 +383,12 @@ void fwd_kernel(FwdParams p) {
     const int row = slot / TL::kChunks;
     const int phys = slot % TL::kChunks;
     cp_row[n] = row;
-    k_src[n] = row * rs_bytes + ((phys ^ TL::k_swz(row)) * 16);
-    v_src[n] = row * rs_bytes + ((phys ^ TL::v_swz(row)) * 16);
+    k_src[n] = row * k_tb + ((phys ^ TL::k_swz(row)) * 16);
+    v_src[n] = row * v_tb + ((phys ^ TL::v_swz(row)) * 16);
   }
-  auto copy_tile = [&](const uint8_t* gsrc, const int (&src)[NPW], int tile_base, int kt) __attribute__((always_inline)) {
+  auto copy_tile = [&](const uint8_t* gsrc, int tb, const int (&src)[NPW], int tile_base, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
-    const uint8_t* g = gsrc + (int64_t)k0 * rs_bytes;
+    const uint8_t* g = gsrc + (int64_t)k0 * tb;
     const uint32_t lds0 = smem_lds + tile_base + gw * NPW * 1024;
     if (k0 + BC <= Nk) {
 #pragma unroll
@@ -374,8 +405,8 @@ void fwd_kernel(FwdParams p) {
       }
     }
   };
-  auto copy_k = [&](int kt) __attribute__((always_inline)) { copy_tile(kg, k_src, (kt & 1) * TILE_BYTES, kt); };
-  auto copy_v = [&](int kt) __attribute__((always_inline)) { copy_tile(vg, v_src, (2 + (kt & 1)) * TILE_BYTES, kt); };
+  auto copy_k = [&](int kt) __attribute__((always_inline)) { copy_tile(kg, k_tb, k_src, (kt & 1) * TILE_BYTES, kt); };
+  auto copy_v = [&](int kt) __attribute__((always_inline)) { copy_tile(vg, v_tb, v_src, (2 + (kt & 1)) * TILE_BYTES, kt); };
 
   // ---- LDS operand addresses of this lane ----
   // K operand (A of S^T = K Q^T): row 32*kb + l32, logical chunk 2*ds + hi.
@@ -420,7 +451,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {   // alternate accumulators
         const bf16x8 a = lds_b128(base + 32 * kb * RB + k_rd[ds]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
+        s[kb] = mfma32<F16>(a, qr[ds], s[kb]);
       }
     }
   };
@@ -437,7 +468,7 @@ void fwd_kernel(FwdParams p) {
           const v4i16 lo = lds_tr(base + r0 + v_rd[b]);
           const v4i16 up = lds_tr(base + r0 + 8 * RB + v_rd[b]);
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], o[b], 0, 0, 0);
+          o[b] = mfma32<F16>(a, pb[kb][t], o[b]);
         }
       }
     }
@@ -483,10 +514,10 @@ void fwd_kernel(FwdParams p) {
     for (int i = 0; i < 2 * N; ++i) {
       if (i < N) {
         const int ds = i / KB, kb = i % KB;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % R], qr[ds], s[kb], 0, 0, 0);
+        s[kb] = mfma32<F16>(ring[i % R], qr[ds], s[kb]);
       } else {
         const int ii = i - N, b = ii % DB, c = ii / DB, kb2 = c / 2, t = c % 2;
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % R], pb[kb2][t], o[b], 0, 0, 0);
+        o[b] = mfma32<F16>(ring[i % R], pb[kb2][t], o[b]);
       }
       if (i + R < 2 * N) ring[i % R] = frag(i + R);
       __builtin_amdgcn_sched_barrier(0);
@@ -554,7 +585,7 @@ void fwd_kernel(FwdParams p) {
           }
           const float e0 = __builtin_amdgcn_exp2f(x0);
           const float e1 = __builtin_amdgcn_exp2f(x1);
-          w[i] = pack_bf16(e0, e1);
+          w[i] = pack2<F16>(e0, e1);
           l_run += e0 + e1;
         }
         pb[kb][t] = __builtin_bit_cast(bf16x8, w);
@@ -641,8 +672,8 @@ void fwd_kernel(FwdParams p) {
     for (int j = kt0; j < js0; ++j) period(j);
     for (int j = js0; j < js1; ++j) {
       if (!group_b) {
-        const uint8_t* gk = kg + (int64_t)((j + 1) * BC) * rs_bytes;
-        const uint8_t* gv = vg + (int64_t)(j * BC) * rs_bytes;
+        const uint8_t* gk = kg + (int64_t)((j + 1) * BC) * k_tb;
+        const uint8_t* gv = vg + (int64_t)(j * BC) * v_tb;
         const uint32_t lk = smem_lds + ((j + 1) & 1) * TILE_BYTES + gw * NPW * 1024;
         const uint32_t lv = smem_lds + (2 + (j & 1)) * TILE_BYTES + gw * NPW * 1024;
         qk_pv(j, [&]() __attribute__((always_inline)) {
@@ -666,15 +697,14 @@ void fwd_kernel(FwdParams p) {
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Nq) {
     const float inv = (BAND && l_tot == 0.f) ? 0.f : __builtin_amdgcn_rcpf(l_tot);
-    uint16_t* orow = p.o + q_off + (int64_t)qrow * rs;
+    uint16_t* orow = p.o + o_off + (int64_t)qrow * o_ts;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(o[b][4 * g + jj] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * hi) = w;
+        const uint2 w = {pack2<F16>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv),
+                         pack2<F16>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
+        *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g + 4 * hi) = w;
       }
     }
     if (hi == 0)

@@ -22,9 +22,11 @@
  *
  * Conventions shared by every entry point.
  *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
- *     by the caller, 16-byte aligned, densely packed (row-major, no strides).
+ *     by the caller, 16-byte aligned, densely packed (row-major, no strides)
+ *     except in the *_strided entry points.
  *     The library keeps no pointer after it returns and allocates no memory.
- *   - Q, K, V and O are bfloat16 (passed as void*); L is float32.
+ *   - Q, K, V and O are bfloat16 (passed as void*), or fp16 where the
+ *     *_strided entry points say so; L is float32.
  *   - Head dimension d must be 32, 64 or 128.
  *   - softmax_scale must be finite and >= 0 (callers normally pass 1/sqrt(d)).
  *   - causal = 1 applies the lower-triangular mask of self-attention (query i
@@ -125,6 +127,63 @@ fa_status fa_fwd_varlen_band(const void* q, const void* k, const void* v, void* 
                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
                              int32_t total, int32_t H, int32_t d, float softmax_scale,
                              int32_t window_left, int32_t window_right, void* stream);
+
+/* Element type of q, k, v and o for the strided entry points. */
+enum {
+  FA_DTYPE_BF16 = 0,
+  FA_DTYPE_F16 = 1
+};
+
+/*
+ * Equal-length batch with any strides and either half-precision type; the
+ * general form of fa_fwd and fa_fwd_band.
+ *   q, o : (B, Nq, H, d) views; k, v: (B, Nk, H, d) views. Element (b, n, h, e)
+ *          of tensor X sits at X + b*X_strides[0] + n*X_strides[1]
+ *          + h*X_strides[2] + e (elements; d is contiguous). Any strides that
+ *          are multiples of 8 (rows 16-byte aligned), with token strides up to
+ *          2^24, are accepted: e.g. the packed (B, S, 3, H, d) QKV tensor passes
+ *          as three views with token stride 3*H*d and head stride d, with no
+ *          copy. Outputs must not overlap each other or the inputs.
+ *   q_strides .. o_strides : HOST int64[3] each: batch, token, head strides.
+ *   lse  : (B, H, Nq) float32, contiguous, written.
+ *   dtype: FA_DTYPE_BF16 or FA_DTYPE_F16 for all of q, k, v and o (fp16
+ *          attention runs on the fp16 matrix cores with fp32 accumulation and
+ *          P rounded to fp16).
+ *   causal / window_left / window_right: causal = 1 with both sides -1 is the
+ *          causal mask (Nq == Nk); causal = 0 with both sides -1 is unmasked;
+ *          causal = 0 with a side >= 0 is the band of fa_fwd_band.
+ *   Source for the two element types and the packed QKV layout:
+ *     "InternViT-6B-448px-V1-2 如何加速注意力计算", section
+ *     FlashAttention 封装类三条执行路径 (fp16/bf16 inputs; the unmasked path
+ *     passes a packed (B, S, 3, H, D) QKV tensor).
+ * Errors: as fa_fwd and fa_fwd_band; a stride that is negative or not a
+ * multiple of 8, a null stride array, an unknown dtype, or causal with a
+ * window side other than -1 is FA_ERR_INVALID_ARGUMENT; a token stride
+ * above 2^24 is FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                         const int64_t* q_strides, const int64_t* k_strides,
+                         const int64_t* v_strides, const int64_t* o_strides, int32_t dtype,
+                         float softmax_scale, int32_t causal, int32_t window_left,
+                         int32_t window_right, void* stream);
+
+/*
+ * Packed variable-length batch with any token and head strides and either
+ * half-precision type; the general form of fa_fwd_varlen and
+ * fa_fwd_varlen_band. Row r (packed token index), head h, element e of
+ * tensor X sits at X + r*X_strides[0] + h*X_strides[1] + e; the stride
+ * arrays are HOST int64[2] (token, head), with the rules of fa_fwd_strided.
+ * cu_seqlens, max_seqlen, total and lse are as in fa_fwd_varlen; dtype and
+ * the mask arguments as in fa_fwd_strided.
+ */
+fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                                int32_t total, int32_t H, int32_t d, const int64_t* q_strides,
+                                const int64_t* k_strides, const int64_t* v_strides,
+                                const int64_t* o_strides, int32_t dtype, float softmax_scale,
+                                int32_t causal, int32_t window_left, int32_t window_right,
+                                void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int32_t status);

@@ -27,14 +27,16 @@ def say(*args):
     sys.stdout.flush()
 
 
-def to_dev(bits: np.ndarray):
+def to_dev(bits: np.ndarray, dtype: str = "bf16"):
+    """16-bit patterns -> a device tensor of that type ('bf16' or 'f16')."""
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
-    return t.view(torch.bfloat16).cuda()
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
 
 
-def to_f64(bits: np.ndarray) -> np.ndarray:
-    return W.bf16_bits_to_f32(bits).astype(np.float64)
+def to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    widen = W.bf16_bits_to_f32 if dtype == "bf16" else W.f16_bits_to_f32
+    return widen(bits).astype(np.float64)
 
 
 def o_to_f64(t) -> np.ndarray:

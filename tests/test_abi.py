@@ -199,3 +199,83 @@ def test_binding_window_arguments():
     assert aa._window((3, 10**12), causal=False) == (3, 2**31 - 1)
     with pytest.raises(ValueError):
         aa.fa_fwd(x, x, x, window=(4, 4))   # host tensors are refused before any window use
+
+
+def _strided(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Nq=100, Nk=80, H=3, d=64,
+             qs=(100 * 3 * 64, 3 * 64, 64), ks=(80 * 3 * 64, 3 * 64, 64),
+             vs=(80 * 3 * 64, 3 * 64, 64), os=(100 * 3 * 64, 3 * 64, 64),
+             dtype=_lib.FA_DTYPE_F16, scale=0.125, causal=0, left=-1, right=-1, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Nq"],
+                                   a["Nk"], a["H"], a["d"], a["qs"], a["ks"], a["vs"], a["os"],
+                                   a["dtype"], a["scale"], a["causal"], a["left"], a["right"],
+                                   a["stream"])
+
+
+def _varlen_strided(**kw):
+    # packed (total, 3, H, d) QKV: token stride 3*H*d, head stride d
+    t = 3 * 2 * 128
+    a = dict(q=P, k=P + 256, v=P + 512, o=P, lse=P, cu=P, num_seqs=2, max_seqlen=100, total=150,
+             H=2, d=128, qs=(t, 128), ks=(t, 128), vs=(t, 128), os=(2 * 128, 128),
+             dtype=_lib.FA_DTYPE_BF16, scale=0.1, causal=1, left=-1, right=-1, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd_varlen_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"],
+                                          a["num_seqs"], a["max_seqlen"], a["total"], a["H"],
+                                          a["d"], a["qs"], a["ks"], a["vs"], a["os"], a["dtype"],
+                                          a["scale"], a["causal"], a["left"], a["right"],
+                                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), INV), (dict(os=None), INV),
+    (dict(qs=(0, 3 * 64 + 4, 64)), INV), (dict(ks=(80 * 3 * 64, 3 * 64, 60)), INV),
+    (dict(vs=(-8, 3 * 64, 64)), INV), (dict(os=(1, 3 * 64, 64)), INV),
+    (dict(ks=(0, (1 << 24) + 8, 64)), UNS),
+    (dict(dtype=2), INV), (dict(dtype=-1), INV),
+    (dict(causal=1), INV),                             # causal needs Nq == Nk
+    (dict(causal=1, Nq=80, left=5), INV),              # causal with a window
+    (dict(causal=2), INV), (dict(left=-2), INV),
+    (dict(d=16), UNS), (dict(q=P + 8), INV), (dict(B=0), INV),
+    (dict(Nq=(1 << 29) + 1, left=3), UNS),
+])
+def test_fa_fwd_strided_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _strided(**kw) == code
+    assert _lib.load().fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), INV), (dict(ks=(3 * 2 * 128, 129)), INV), (dict(dtype=7), INV),
+    (dict(causal=1, right=0), INV), (dict(cu=None), INV), (dict(d=256), UNS),
+])
+def test_fa_fwd_varlen_strided_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _varlen_strided(**kw) == code
+
+
+def test_strided_valid_calls_without_a_device_are_hip_errors():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _strided() == HIP                                   # fp16, unmasked
+    assert _strided(dtype=_lib.FA_DTYPE_BF16, causal=1, Nq=80) == HIP
+    assert _strided(left=0, right=7) == HIP                     # band
+    assert _strided(qs=(0, 0, 0)) == HIP                        # zero strides are allowed
+    assert _varlen_strided() == HIP
+    assert _varlen_strided(total=0, max_seqlen=0) == _lib.FA_OK
+
+
+def test_binding_accepts_f16_and_views_but_not_bad_ones():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 8, 1, 32, dtype=torch.float16)
+    with pytest.raises(ValueError):            # host tensors are refused
+        aa.fa_fwd(x, x, x)
+    with pytest.raises(TypeError):             # neither bf16 nor fp16 (checked first)
+        aa.fa_fwd(x.float(), x.float(), x.float())
+    qkv = torch.zeros(2, 5, 3, 4, 32)          # packed (B, S, 3, H, d)
+    assert aa._strides(qkv[:, :, 1]) == [5 * 3 * 4 * 32, 3 * 4 * 32, 32]
+    assert aa._strides(torch.zeros(1, 5, 1, 32)) == [0, 32, 0]
+    assert aa._dtype_code(torch.float16) == _lib.FA_DTYPE_F16
+    assert aa._dtype_code(torch.bfloat16) == _lib.FA_DTYPE_BF16

@@ -86,3 +86,28 @@ def test_band_pair_count():
                         p = i + Nk - Nq
                         n += (left is None or j >= p - left) and (right is None or j <= p + right)
                 assert W.band_pairs(Nq, Nk, window) == n, (Nq, Nk, window)
+
+
+def test_f16_rne_hand_picked():
+    x = np.array([1.0, 65504.0, 1 / 3, 2.0**-24, 1 + 2.0**-11, 1 + 3 * 2.0**-11, -2.5, 0.0],
+                 dtype=np.float32)
+    want = [0x3C00, 0x7BFF, 0x3555, 0x0001, 0x3C00, 0x3C02, 0xC100, 0x0000]
+    assert W.f32_to_f16_bits(x).tolist() == want
+    assert np.array_equal(W.f16_bits_to_f32(np.array(want, dtype=np.uint16))[[0, 1, 6]],
+                          np.array([1.0, 65504.0, -2.5], dtype=np.float32))
+
+
+def test_f16_matches_torch_conversion():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(7).standard_normal(10000).astype(np.float32) * 50
+    ours = W.f32_to_f16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+def test_dense_f16_takes_the_same_draws():
+    qb, kb, vb = W.make_dense(1, 9, 2, 32, seed=5)
+    qh, kh, vh = W.make_dense(1, 9, 2, 32, seed=5, dtype="f16")
+    # both round the same float32 draws: they agree to bf16 precision
+    assert np.allclose(W.bf16_bits_to_f32(qb), W.f16_bits_to_f32(qh), rtol=2**-7, atol=1e-6)
+    assert not np.array_equal(qb, qh)

@@ -26,7 +26,8 @@ Recipe for every draw: numpy.random.default_rng(seed); float32
 standard_normal in C order, drawn in the order lengths (varlen only) -> Q ->
 K -> V; then rounded to bfloat16 with round-to-nearest-even. For "vit", Q and
 K are RMS-normalised over d in float32 (eps 1e-6, unit weight) before the
-rounding; V is not.
+rounding; V is not. fp16 inputs (dtype "f16") take the same float32 draws
+rounded to IEEE binary16 (round to nearest, ties to even) instead.
 """
 from __future__ import annotations
 
@@ -148,9 +149,29 @@ def _draw(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(size=shape, dtype=np.float32)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's conversion: round to
+    nearest, ties to even); returns the 16-bit patterns as uint16."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen binary16 bit patterns (uint16) to float32 exactly."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def _round(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return f32_to_f16_bits(x)
+    raise ValueError(f"dtype must be 'bf16' or 'f16' (got {dtype!r})")
+
+
 def make_dense(B: int, N: int, H: int, d: int, seed: int, rms_qk: bool = False,
-               Nk: int | None = None):
-    """Return (q, k, v) as uint16 bf16 bit patterns, q (B,N,H,d), k/v (B,Nk,H,d)."""
+               Nk: int | None = None, dtype: str = "bf16"):
+    """Return (q, k, v) as uint16 bit patterns of dtype ('bf16' or 'f16'),
+    q (B,N,H,d), k/v (B,Nk,H,d)."""
     Nk = N if Nk is None else Nk
     rng = np.random.default_rng(seed)
     q = _draw(rng, (B, N, H, d))
@@ -159,7 +180,7 @@ def make_dense(B: int, N: int, H: int, d: int, seed: int, rms_qk: bool = False,
     if rms_qk:
         q = _rms_normalise(q)
         k = _rms_normalise(k)
-    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    return _round(q, dtype), _round(k, dtype), _round(v, dtype)
 
 
 def varlen_lengths(num_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
@@ -177,8 +198,9 @@ def cu_seqlens_from_lengths(lengths) -> np.ndarray:
     return cu.astype(np.int32)
 
 
-def make_varlen(lengths, H: int, d: int, seed: int, rng: np.random.Generator | None = None):
-    """Return (q, k, v, cu_seqlens): q/k/v (total,H,d) bf16 bits, cu int32."""
+def make_varlen(lengths, H: int, d: int, seed: int, rng: np.random.Generator | None = None,
+                dtype: str = "bf16"):
+    """Return (q, k, v, cu_seqlens): q/k/v (total,H,d) bits of dtype, cu int32."""
     cu = cu_seqlens_from_lengths(lengths)
     total = int(cu[-1])
     if rng is None:
@@ -186,7 +208,7 @@ def make_varlen(lengths, H: int, d: int, seed: int, rng: np.random.Generator | N
     q = _draw(rng, (total, H, d))
     k = _draw(rng, (total, H, d))
     v = _draw(rng, (total, H, d))
-    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v), cu
+    return _round(q, dtype), _round(k, dtype), _round(v, dtype), cu
 
 
 def make_workload(name: str):
