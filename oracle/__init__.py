@@ -11,10 +11,15 @@ Contents:
                 with the score matrix materialised, in float64.
   tiled.py      the blockwise online-softmax forward exactly as the pages lay
                 it out, in float64, used only to cross-check the definition.
+  backward.py   the gradients dQ, dK, dV of the definition (chain rule through
+                the softmax), with P materialised, in float64.
 """
 from .attention import (attention, attention_probs, attention_dense,
                         attention_varlen, ORACLE_DTYPE)
+from .backward import (attention_backward, attention_backward_dense,
+                       attention_backward_varlen)
 from .tiled import attention_tiled
 
 __all__ = ["attention", "attention_probs", "attention_dense", "attention_varlen",
-           "attention_tiled", "ORACLE_DTYPE"]
+           "attention_tiled", "attention_backward", "attention_backward_dense",
+           "attention_backward_varlen", "ORACLE_DTYPE"]

@@ -115,3 +115,49 @@ def test_causal_requires_square():
 def test_empty_query():
     O, L = attention(np.zeros((0, 4)), np.zeros((3, 4)), np.zeros((3, 4)), 1.0, False)
     assert O.shape == (0, 4) and L.shape == (0,)
+
+
+# ---------------------------------------------------------------------------
+# Backward (gradients of the definition)
+# ---------------------------------------------------------------------------
+
+from oracle import (attention_backward, attention_backward_dense,  # noqa: E402
+                    attention_backward_varlen)
+from tests.oracle_bwd_pins import BWD_PINS  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
+def test_oracle_backward_pins(pin):
+    pin(attention_backward)
+
+
+def test_backward_p_recomputed_from_l():
+    """The pages' recomputation: with L from the forward, exp(S - L) is the
+    softmax P the backward uses."""
+    rng = np.random.default_rng(31)
+    q, k = rng.standard_normal((6, 4)), rng.standard_normal((6, 4))
+    for causal in (False, True):
+        _, L = attention(q, k, rng.standard_normal((6, 2)), 0.8, causal)
+        S = 0.8 * q @ k.T
+        if causal:
+            S = np.where(np.triu(np.ones((6, 6), dtype=bool), 1), -np.inf, S)
+        np.testing.assert_allclose(np.exp(S - L[:, None]), attention_probs(q, k, 0.8, causal),
+                                   rtol=0, atol=1e-14)
+
+
+def test_backward_wrappers_match_single_head():
+    rng = np.random.default_rng(32)
+    q, k, v, do = (rng.standard_normal((2, 7, 3, 4)) for _ in range(4))
+    dq, dk, dv, delta = attention_backward_dense(q, k, v, do, 0.5, True)
+    for b in range(2):
+        for h in range(3):
+            g = attention_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], 0.5, True)
+            for got, want in zip((dq[b, :, h], dk[b, :, h], dv[b, :, h], delta[b, h]), g):
+                np.testing.assert_array_equal(got, want)
+    lengths = [3, 0, 5]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    qv, kv, vv, dov = (rng.standard_normal((8, 2, 4)) for _ in range(4))
+    dq, dk, dv, delta = attention_backward_varlen(qv, kv, vv, dov, cu, 0.5, False)
+    g = attention_backward(qv[3:8, 1], kv[3:8, 1], vv[3:8, 1], dov[3:8, 1], 0.5, False)
+    np.testing.assert_array_equal(dk[3:8, 1], g[1])
+    np.testing.assert_array_equal(delta[1, 3:8], g[3])

@@ -153,3 +153,67 @@ def test_band_mutant_is_caught(mutation):
         except Exception:  # noqa: BLE001 - any failure counts as caught
             failed.append(pin.__name__)
     assert failed, f"band mutation {mutation!r} passed every band pin"
+
+
+# ---------------------------------------------------------------------------
+# Backward: planted mistakes in a copy of the gradient formulas must each fail
+# at least one backward pin.
+# ---------------------------------------------------------------------------
+
+from tests.oracle_bwd_pins import BWD_PINS  # noqa: E402
+
+BWD_MUTATIONS = ["dq_no_scale", "dk_no_scale", "ds_sign_flipped", "delta_dropped",
+                 "delta_from_p_only", "dk_from_ds_not_transposed", "dv_from_p_not_transposed",
+                 "dq_uses_v", "causal_mask_dropped", "delta_from_unmasked_p"]
+
+
+def _make_bwd(mutation):
+    def fn(q, k, v, do, scale, causal):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        Nq, Nk = q.shape[0], k.shape[0]
+        S = scale * (q @ k.T)
+        mask = np.triu(np.ones((Nq, Nk), dtype=bool), 1) if causal else np.zeros((Nq, Nk), bool)
+        Sm = S if mutation == "causal_mask_dropped" else np.where(mask, -np.inf, S)
+        P = np.exp(Sm - Sm.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dv = (P @ do[:Nk] if Nq >= Nk else P.T @ do) if mutation == "dv_from_p_not_transposed" \
+            else P.T @ do
+        dP = do @ v.T
+        if mutation == "delta_from_unmasked_p":
+            Pu = np.exp(S - S.max(axis=1, keepdims=True))
+            Pu /= Pu.sum(axis=1, keepdims=True)
+            delta = np.sum(Pu * dP, axis=1)
+        elif mutation == "delta_from_p_only":
+            delta = np.sum(P, axis=1)
+        else:
+            delta = np.sum(P * dP, axis=1)
+        dS = P * (dP - (0.0 if mutation == "delta_dropped" else delta[:, None]))
+        if mutation == "ds_sign_flipped":
+            dS = -dS
+        dq = (1.0 if mutation == "dq_no_scale" else scale) * (dS @ (v if mutation == "dq_uses_v" else k))
+        if mutation == "dk_from_ds_not_transposed":
+            dk = scale * (dS @ q[:Nk] if Nq >= Nk and dS.shape[1] == Nk else dS.T @ q)
+            if Nq == Nk:
+                dk = scale * (dS @ q)
+        else:
+            dk = (1.0 if mutation == "dk_no_scale" else scale) * (dS.T @ q)
+        return dq, dk, dv, delta
+    return fn
+
+
+def test_bwd_reference_copy_passes():
+    fn = _make_bwd("none")
+    for pin in BWD_PINS:
+        pin(fn)
+
+
+@pytest.mark.parametrize("mutation", BWD_MUTATIONS)
+def test_bwd_mutant_is_caught(mutation):
+    fn = _make_bwd(mutation)
+    failed = []
+    for pin in BWD_PINS:
+        try:
+            pin(fn)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(pin.__name__)
+    assert failed, f"backward mutation {mutation!r} passed every backward pin"
