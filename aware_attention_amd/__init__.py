@@ -20,6 +20,12 @@ library is missing or the device is not a gfx950, calls raise.
     strides are multiples of 8 elements, such as q = qkv[:, :, 0] of a packed
     (B, S, 3, H, d) tensor; such calls go through fa_fwd_strided /
     fa_fwd_varlen_strided with no copy.
+    dq, dk, dv, delta = fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False)
+    dq, dk, dv, delta = fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, ...)
+        the backward (contiguous tensors of one half-precision type): S and P are
+        recomputed from lse; delta = rowsum(dout * o), laid out like lse.
+    o = attention(q, k, v, softmax_scale=None, causal=False)
+        forward with autograd: o.backward(...) runs fa_bwd.
 
 The default scale is 1/sqrt(d), as in the definition on "FlashAttention/zh"
 (marovi.ai wiki), section 為何標準注意力運行緩慢. Only half precision on the
@@ -32,12 +38,12 @@ from __future__ import annotations
 import math
 
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
-                   FA_ERR_UNSUPPORTED, FA_OK, FaError, check, load, raw_fa_fwd, raw_fa_fwd_band,
-                   raw_fa_fwd_strided, raw_fa_fwd_varlen, raw_fa_fwd_varlen_band,
-                   raw_fa_fwd_varlen_strided)
+                   FA_ERR_UNSUPPORTED, FA_OK, FaError, check, load, raw_fa_bwd, raw_fa_bwd_varlen,
+                   raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_strided, raw_fa_fwd_varlen,
+                   raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
 
-__all__ = ["fa_fwd", "fa_fwd_varlen", "FaError", "load", "FA_OK", "FA_ERR_INVALID_ARGUMENT",
-           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "attention", "FaError", "load",
+           "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
 
 
 def _torch():
@@ -176,3 +182,112 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=Fa
             check(raw_fa_fwd_varlen_band(*ptrs, num_seqs, int(max_seqlen), total, H, d, scale,
                                          wl, wr, stream))
     return out, lse
+
+
+def _check_contiguous(ts, names, dtype):
+    for t, n in zip(ts, names):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous for the backward")
+        if t.dtype != dtype:
+            raise TypeError(f"{n} must be {dtype} like q (got {t.dtype})")
+
+
+def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None,
+           delta=None):
+    """Backward over an equal-length batch; returns (dq, dk, dv, delta)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check_tensor(t, n, 4)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != d \
+            or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o and dout")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_contiguous((q, k, v, o, dout, dq, dk, dv), ("q", "k", "v", "o", "dout", "dq", "dk", "dv"),
+                      q.dtype)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk and dv must be shaped like q, k and v")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        if t.shape != (B, H, Nq) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 tensor of shape (B, H, Nq)")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        check(raw_fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         delta.data_ptr(), B, Nq, Nk, H, d, _dtype_code(q.dtype),
+                         _scale(softmax_scale, d), int(bool(causal)), stream))
+    return dq, dk, dv, delta
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
+                  causal=False, dq=None, dk=None, dv=None, delta=None):
+    """Backward over a packed variable-length batch; returns (dq, dk, dv, delta)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check_tensor(t, n, 3)
+    total, H, d = q.shape
+    if any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o and dout must share the packed shape (total, H, d)")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
+            or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    _check_contiguous((q, k, v, o, dout, dq, dk, dv), ("q", "k", "v", "o", "dout", "dq", "dk", "dv"),
+                      q.dtype)
+    if any(t.shape != q.shape for t in (dq, dk, dv)):
+        raise ValueError("dq, dk and dv must be shaped like q")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        if t.shape != (H, total) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 tensor of shape (H, total)")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        check(raw_fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), delta.data_ptr(), cu_seqlens.data_ptr(),
+                                cu_seqlens.numel() - 1, int(max_seqlen), total, H, d,
+                                _dtype_code(q.dtype), _scale(softmax_scale, d),
+                                int(bool(causal)), stream))
+    return dq, dk, dv, delta
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, softmax_scale, causal):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            o, lse = fa_fwd(q, k, v, softmax_scale=softmax_scale, causal=causal)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.softmax_scale, ctx.causal = softmax_scale, causal
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, dout.contiguous(),
+                                   softmax_scale=ctx.softmax_scale, causal=ctx.causal)
+            return dq, dk, dv, None, None
+
+    return _Attention
+
+
+_ATTENTION_FN = None
+
+
+def attention(q, k, v, softmax_scale=None, causal=False):
+    """o = softmax(scale q k^T) v over (B, N, H, d) tensors, differentiable: the
+    forward is fa_fwd and the backward fa_bwd (both HIP kernels)."""
+    global _ATTENTION_FN
+    if _ATTENTION_FN is None:
+        _ATTENTION_FN = _autograd_function()
+    return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal)

@@ -18,7 +18,8 @@ FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
-            "fa_fwd_varlen_strided", "fa_status_string", "fa_last_error", "fa_abi_version")
+            "fa_fwd_varlen_strided", "fa_bwd", "fa_bwd_varlen", "fa_status_string",
+            "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -57,6 +58,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen_strided.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, p64, p64,
                                           p64, p64, i32, f32, i32, i32, i32, vp]
     lib.fa_fwd_varlen_strided.restype = i32
+    lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_varlen.argtypes = [vp] * 11 + [i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_bwd_varlen.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -123,3 +128,17 @@ def raw_fa_fwd_varlen_strided(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, 
                                         _int64_array(q_strides), _int64_array(k_strides),
                                         _int64_array(v_strides), _int64_array(o_strides), dtype,
                                         scale, causal, window_left, window_right, stream)
+
+
+def raw_fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype, scale, causal,
+               stream) -> int:
+    """Pointer-level call of fa_bwd; returns the status code."""
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype, scale,
+                         causal, stream)
+
+
+def raw_fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs, max_seqlen, total, H,
+                      d, dtype, scale, causal, stream) -> int:
+    """Pointer-level call of fa_bwd_varlen; returns the status code."""
+    return load().fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs,
+                                max_seqlen, total, H, d, dtype, scale, causal, stream)

@@ -21,25 +21,52 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def hipcc_command(out: str = LIB, extra=()) -> list[str]:
-    return [HIPCC, *DEVICE_FLAGS, "-fPIC", "-shared", "-Wall",
+# Translation units of libfa.so: the forward entry points and host helpers,
+# and the backward entry points. They compile in parallel, then link.
+SOURCES = ["fa_api.hip", "fa_bwd_api.hip"]
+_NOISE = "is not a recognized feature for this target"
+
+
+def hipcc_compile(src: str, obj: str, extra=()) -> list[str]:
+    return [HIPCC, *DEVICE_FLAGS, "-fPIC", "-c", "-Wall",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            os.path.join(CSRC, "fa_api.hip"), "-o", out, *extra]
+            os.path.join(CSRC, src), "-o", obj, *extra]
+
+
+def _messages(res) -> list[str]:
+    return [ln for ln in (res.stdout + res.stderr).splitlines() if _NOISE not in ln]
 
 
 def build(verbose: bool = True) -> str:
+    objs = [os.path.join(CSRC, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [hipcc_compile(s, o) for s, o in zip(SOURCES, objs)]
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print("[build]", " ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                      text=True))
+    failed = []
+    for cmd, proc in zip(cmds, procs):
+        out, err = proc.communicate()
+        res = subprocess.CompletedProcess(cmd, proc.returncode, out, err)
+        msgs = _messages(res)
+        if res.returncode != 0:
+            failed.append("\n".join(msgs))
+        elif verbose and msgs:
+            print("\n".join(msgs), flush=True)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp]
     if verbose:
-        print("[build]", " ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+        print("[build]", " ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs), flush=True)
+        raise RuntimeError("hipcc link failed:\n" + "\n".join(_messages(res)))
     os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
     return LIB
 
 

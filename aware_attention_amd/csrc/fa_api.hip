@@ -11,8 +11,9 @@
 #include <string>
 
 #include "fa_fwd_kernel.hpp"
+#include "fa_host.hpp"
 
-namespace {
+namespace fa_host {
 
 thread_local std::string g_last_error;
 
@@ -52,6 +53,15 @@ fa_status check_device() {
   if (!info.supported) return fail(FA_ERR_UNSUPPORTED, "libfa runs on gfx950 only; device is " + info.arch);
   return FA_OK;
 }
+
+}  // namespace fa_host
+
+namespace {
+
+using fa_host::aligned16;
+using fa_host::check_device;
+using fa_host::fail;
+using fa_host::g_last_error;
 
 template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16>
 hipError_t launch_one(const fa::FwdParams& p, uint32_t grid, hipStream_t stream) {

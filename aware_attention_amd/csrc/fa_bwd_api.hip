@@ -1,0 +1,190 @@
+// C ABI of the backward pass (fa_bwd, fa_bwd_varlen): argument checks and
+// the three launches. The operation is documented in include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "fa.h"
+#include "fa_bwd_kernel.hpp"
+#include "fa_host.hpp"
+
+namespace {
+
+using fa_host::aligned16;
+using fa_host::check_device;
+using fa_host::fail;
+
+template <int D, bool CAUSAL, bool VARLEN, bool F16>
+hipError_t launch_bwd_t(const fa::BwdParams& p, int64_t nrows, int N, uint32_t grid_k,
+                        uint32_t grid_q, hipStream_t stream) {
+  hipLaunchKernelGGL((fa::delta_kernel<D, F16>), dim3((uint32_t)((nrows + 255) / 256)), dim3(256),
+                     0, stream, p.o, p.dout, p.delta, nrows, p.H, N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16>), dim3(grid_k), dim3(fa::kBwdThreads),
+                     0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  fa::BwdParams pq = p;
+  pq.n_tiles = (int32_t)(grid_q / (uint32_t)(p.H * p.nbatch));
+  hipLaunchKernelGGL((fa::dq_kernel<D, CAUSAL, VARLEN, F16>), dim3(grid_q), dim3(fa::kBwdThreads),
+                     0, stream, pq);
+  return hipGetLastError();
+}
+
+template <bool CAUSAL, bool VARLEN, bool F16>
+hipError_t launch_bwd_d(const fa::BwdParams& p, int d, int64_t nrows, int N, uint32_t grid_k,
+                        uint32_t grid_q, hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_bwd_t<32, CAUSAL, VARLEN, F16>(p, nrows, N, grid_k, grid_q, stream);
+    case 64: return launch_bwd_t<64, CAUSAL, VARLEN, F16>(p, nrows, N, grid_k, grid_q, stream);
+    default: return launch_bwd_t<128, CAUSAL, VARLEN, F16>(p, nrows, N, grid_k, grid_q, stream);
+  }
+}
+
+template <bool VARLEN>
+hipError_t launch_bwd(const fa::BwdParams& p, int d, int32_t dtype, bool causal, int64_t nrows,
+                      int N, uint32_t grid_k, uint32_t grid_q, hipStream_t stream) {
+  const bool f16 = dtype == FA_DTYPE_F16;
+  if (causal)
+    return f16 ? launch_bwd_d<true, VARLEN, true>(p, d, nrows, N, grid_k, grid_q, stream)
+               : launch_bwd_d<true, VARLEN, false>(p, d, nrows, N, grid_k, grid_q, stream);
+  return f16 ? launch_bwd_d<false, VARLEN, true>(p, d, nrows, N, grid_k, grid_q, stream)
+             : launch_bwd_d<false, VARLEN, false>(p, d, nrows, N, grid_k, grid_q, stream);
+}
+
+fa_status check_bwd_common(int32_t H, int32_t d, int32_t dtype, float scale, int32_t causal) {
+  if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+    return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
+  if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
+  return FA_OK;
+}
+
+bool all_aligned(const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (!ptrs[i] || !aligned16(ptrs[i])) return false;
+  return true;
+}
+
+constexpr float kLog2eHost = 1.44269504088896340736f;
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
+                 int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
+                 float softmax_scale, int32_t causal, void* stream) {
+  fa_host::g_last_error.clear();
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+  for (const void* x : ptrs)
+    if (!x) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (B < 1 || Nq < 1 || Nk < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B, Nq and Nk must be >= 1");
+  fa_status st = check_bwd_common(H, d, dtype, softmax_scale, causal);
+  if (st != FA_OK) return st;
+  if (causal && Nq != Nk) return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
+  if (!all_aligned(ptrs, 10)) return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const int64_t units = (int64_t)H * B;
+  const int64_t grid_k = (Nk + fa::kBwdRows - 1) / fa::kBwdRows * units;
+  const int64_t grid_q = (Nq + fa::kBwdRows - 1) / fa::kBwdRows * units;
+  const int64_t nrows = (int64_t)B * Nq * H;
+  if (grid_k > INT32_MAX || grid_q > INT32_MAX || (nrows + 255) / 256 > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.cu_seqlens = nullptr;
+  p.row_stride = (int64_t)H * d;
+  p.q_batch_stride = (int64_t)Nq * H * d;
+  p.k_batch_stride = (int64_t)Nk * H * d;
+  p.lse_batch_stride = (int64_t)H * Nq;
+  p.lse_head_stride = Nq;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.H = H;
+  p.nbatch = B;
+  p.n_tiles = (int32_t)(grid_k / units);
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * kLog2eHost;
+  const hipError_t e = launch_bwd<false>(p, d, dtype, causal == 1, nrows, Nq, (uint32_t)grid_k,
+                                         (uint32_t)grid_q, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
+                        float softmax_scale, int32_t causal, void* stream) {
+  fa_host::g_last_error.clear();
+  if (!cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
+  if (num_seqs < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
+  if (total < 0 || max_seqlen < 0) return fail(FA_ERR_INVALID_ARGUMENT, "total and max_seqlen must be >= 0");
+  if (max_seqlen > total) return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen exceeds total");
+  fa_status st = check_bwd_common(H, d, dtype, softmax_scale, causal);
+  if (st != FA_OK) return st;
+  if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+  for (const void* x : ptrs)
+    if (!x) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (!all_aligned(ptrs, 10) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned (cu_seqlens 4-byte)");
+  const int64_t units = (int64_t)H * num_seqs;
+  const int64_t n_t = (max_seqlen + fa::kBwdRows - 1) / fa::kBwdRows;
+  const int64_t grid = n_t * units;
+  const int64_t nrows = (int64_t)total * H;
+  if (grid > INT32_MAX || (nrows + 255) / 256 > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.cu_seqlens = cu_seqlens;
+  p.row_stride = (int64_t)H * d;
+  p.q_batch_stride = 0;
+  p.k_batch_stride = 0;
+  p.lse_batch_stride = 0;
+  p.lse_head_stride = total;
+  p.Nq = 0;
+  p.Nk = 0;
+  p.H = H;
+  p.nbatch = num_seqs;
+  p.n_tiles = (int32_t)n_t;
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * kLog2eHost;
+  const hipError_t e = launch_bwd<true>(p, d, dtype, causal == 1, nrows, total, (uint32_t)grid,
+                                        (uint32_t)grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,414 @@
+// FlashAttention-2 backward for gfx950 (CDNA4): device code.
+//
+// The backward recomputes the scores S and the probabilities P from the
+// saved log-sum-exp L instead of storing P ("FlashAttention/zh" (marovi.ai
+// wiki), section 反向傳遞與重計算): P_ij = exp(scale q_i.k_j - L_i). With the
+// incoming gradient dO, the chain rule through the softmax gives
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = dO_i . O_i,
+//   dQ = scale dS K,   dK = scale dS^T Q.
+// Three kernels, run in this order on one stream:
+//   * delta_kernel: D_i = sum_e dO_ie O_ie in fp32, one row per lane;
+//   * dkdv_kernel:  one workgroup per 128 keys of one (batch or sequence,
+//     head); each lane owns one key, with its K and V rows in VGPRs; 64-query
+//     tiles of Q and dO stream through LDS. Per tile: S = Q K^T and
+//     dP = dO V^T on the matrix cores (keys in the accumulator columns), P and
+//     dS in registers, then dV^T += dO^T P and dK^T += Q^T dS, whose A
+//     operands are transposing LDS reads of the same Q and dO tiles;
+//   * dq_kernel:    one workgroup per 128 queries; each lane owns one query
+//     (Q and dO rows in VGPRs, L and D lane-local); 64-key tiles of K and V
+//     stream through LDS. Per tile: S^T = K Q^T and dP^T = V dO^T, dS^T in
+//     registers, then dQ^T += K^T dS^T (A operand: transposing reads of K).
+// dQ is produced by its own pass over the keys (S and dP recomputed once more)
+// instead of by atomic adds, so the library needs no accumulation buffer.
+//
+// Operand layouts are those of the forward (v_mfma_f32_32x32x16, wave64):
+// accumulator lane l, register r holds D[8(r/4) + 4(l/32) + r%4][l%32], and
+// registers 8t..8t+7 of a 32-row block, packed to 16 bits, are the B operand
+// of a 16-row k-step whose A operand comes from ds_read_b64_tr_b16 at rows
+// {0..3, 8..11} + 4(l/32) of that step (the same permutation on both sides).
+// LDS tiles are row-major with rows padded by 16 bytes.
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;            // natural-log L from the forward
+  float* delta;                // D, laid out like lse
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* cu_seqlens;   // varlen only
+  int64_t row_stride;          // elements between tokens: H * d (all tensors)
+  int64_t q_batch_stride;      // dense: Nq * H * d (q, o, dout, dq)
+  int64_t k_batch_stride;      // dense: Nk * H * d (k, v, dk, dv)
+  int64_t lse_batch_stride;    // dense: H * Nq; varlen: 0
+  int64_t lse_head_stride;     // dense: Nq; varlen: total
+  int32_t Nq;                  // dense only
+  int32_t Nk;                  // dense only
+  int32_t H;
+  int32_t nbatch;              // B or num_seqs
+  int32_t n_tiles;             // 128-row tiles per unit in this launch
+  float scale;                 // softmax scale
+  float scale_log2;            // scale * log2(e)
+};
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;   // rows a workgroup owns
+constexpr int kBwdTile = 64;               // rows of a streamed LDS tile
+constexpr float kLog2eF = 1.44269504088896340736f;
+
+template <bool F16>
+__device__ __forceinline__ float half_to_float(uint16_t b) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, b);
+  else return __uint_as_float((uint32_t)b << 16);
+}
+
+// D_i = dO_i . O_i for every row (token, head) of the launch, one row per
+// thread. Rows are numbered in memory order, row = token * H + head, with
+// token = b * N + n (dense) or the packed index (varlen, B = 1, N = total).
+template <int D, bool F16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                  float* __restrict__ delta, int64_t nrows, int H, int N) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= nrows) return;
+  const u32x4* a = reinterpret_cast<const u32x4*>(o + row * D);
+  const u32x4* b = reinterpret_cast<const u32x4*>(dout + row * D);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 x = a[c], y = b[c];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(half_to_float<F16>((uint16_t)(x[w] & 0xffff)),
+                           half_to_float<F16>((uint16_t)(y[w] & 0xffff)), acc);
+      acc = __builtin_fmaf(half_to_float<F16>((uint16_t)(x[w] >> 16)),
+                           half_to_float<F16>((uint16_t)(y[w] >> 16)), acc);
+    }
+  }
+  const int64_t token = row / H;
+  const int head = (int)(row - token * H);
+  const int64_t bidx = token / N;
+  const int64_t n = token - bidx * N;
+  delta[(bidx * H + head) * N + n] = acc;
+}
+
+// Row-major LDS tile of kBwdTile rows, rows padded to 2 D + 16 bytes; rows
+// at or past nvalid are zero.
+template <int D>
+__device__ __forceinline__ void load_rows(uint8_t* lds, const uint16_t* g, int64_t rs, int row0,
+                                          int nvalid, int tid) {
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int RBP = 2 * D + 16;
+#pragma unroll
+  for (int c = tid; c < kBwdTile * CH; c += kBwdThreads) {
+    const int r = c / CH, ch = c % CH;
+    u32x4 val = {0, 0, 0, 0};
+    if (row0 + r < nvalid) val = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * rs + ch * 8);
+    *reinterpret_cast<u32x4*>(lds + r * RBP + ch * 16) = val;
+  }
+}
+
+// Operand access of one lane into a padded tile (see the file comment).
+template <int D>
+struct BwdLanes {
+  static constexpr int RBP = 2 * D + 16;
+  int row_rd;        // row-major A fragment: row l%32, 16 bytes at chunk 2 ds + l/32
+  int tr_rd[D / 32]; // transposed A fragment of 32-column block b
+  __device__ BwdLanes(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5, vg16 = lane >> 4, vi = lane & 15;
+    row_rd = l32 * RBP + hi * 16;
+    const int v_row = 4 * hi + (vi >> 2);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) tr_rd[b] = v_row * RBP + (32 * b + 16 * (vg16 & 1) + 4 * (vi & 3)) * 2;
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds16(const uint8_t* smem, int byte) {
+  return *reinterpret_cast<const bf16x8*>(smem + byte);
+}
+__device__ __forceinline__ bf16x8 lds_tr8(const uint8_t* smem, int byte, int byte_up) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint8_t*)smem + byte));
+  const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint8_t*)smem + byte_up));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Work item of a workgroup: (128-row tile, head, batch or sequence) with the
+// tile index taken from blockIdx.x / units; offsets of the unit's rows.
+struct BwdUnit {
+  int tile, head, bidx, Nq, Nk;
+  int64_t q_off, k_off, l_off;
+};
+
+__device__ __forceinline__ BwdUnit bwd_unit(const BwdParams& p, bool varlen, int D) {
+  BwdUnit u;
+  const int per = p.H * p.nbatch;
+  u.tile = blockIdx.x / per;
+  const int rem = blockIdx.x - u.tile * per;
+  u.head = rem % p.H;
+  u.bidx = rem / p.H;
+  if (varlen) {
+    const int start = p.cu_seqlens[u.bidx];
+    const int len = p.cu_seqlens[u.bidx + 1] - start;
+    u.Nq = len;
+    u.Nk = len;
+    u.q_off = (int64_t)start * p.row_stride + (int64_t)u.head * D;
+    u.k_off = u.q_off;
+    u.l_off = (int64_t)u.head * p.lse_head_stride + start;
+  } else {
+    u.Nq = p.Nq;
+    u.Nk = p.Nk;
+    u.q_off = (int64_t)u.bidx * p.q_batch_stride + (int64_t)u.head * D;
+    u.k_off = (int64_t)u.bidx * p.k_batch_stride + (int64_t)u.head * D;
+    u.l_off = (int64_t)u.bidx * p.lse_batch_stride + (int64_t)u.head * p.lse_head_stride;
+  }
+  return u;
+}
+
+// Store a 32-row x D block held transposed in accumulators (lane = row,
+// registers = columns 32 b + 8 g + 4 (l/32) + 0..3), times `mul`.
+template <int D, bool F16>
+__device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16 (&acc)[D / 32], float mul,
+                                           int hi) {
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint2 w = {pack2<F16>(acc[b][4 * g] * mul, acc[b][4 * g + 1] * mul),
+                       pack2<F16>(acc[b][4 * g + 2] * mul, acc[b][4 * g + 3] * mul)};
+      *reinterpret_cast<uint2*>(row + 32 * b + 8 * g + 4 * hi) = w;
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN, bool F16>
+__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
+                          amdgpu_waves_per_eu(1, 1)))
+void dkdv_kernel(BwdParams p) {
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int RBP = 2 * D + 16;
+  constexpr int TB = kBwdTile * RBP;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB + 2 * kBwdTile * 4];
+  uint8_t* q_lds = smem;
+  uint8_t* do_lds = smem + TB;
+  float* l_lds = reinterpret_cast<float*>(smem + 2 * TB);   // L * log2(e) per query
+  float* d_lds = l_lds + kBwdTile;                          // D per query
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  // Causal: key tiles in ascending order see the most queries first.
+  const BwdUnit u = bwd_unit(p, VARLEN, D);
+  const int k0 = u.tile * kBwdRows;
+  if (k0 >= u.Nk) return;
+  const int rs = (int)p.row_stride;
+  const int kw0 = k0 + wave * 32;
+  const int krow = kw0 + l32;
+
+  bf16x8 kr[DS], vr[DS];
+  if (krow < u.Nk) {
+    const u32x4* ks = reinterpret_cast<const u32x4*>(p.k + u.k_off + (int64_t)krow * rs);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(p.v + u.k_off + (int64_t)krow * rs);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kr[s] = __builtin_bit_cast(bf16x8, ks[2 * s + hi]);
+      vr[s] = __builtin_bit_cast(bf16x8, vs[2 * s + hi]);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kr[s] = vr[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  const BwdLanes<D> ln(lane);
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) dk[b] = dv[b] = f32x16{};
+
+  const int n_qt = (u.Nq + kBwdTile - 1) / kBwdTile;
+  const int qt0 = CAUSAL ? k0 / kBwdTile : 0;
+  const bool wave_has = kw0 < u.Nk;
+  for (int qt = qt0; qt < n_qt; ++qt) {
+    const int qb0 = qt * kBwdTile;
+    __syncthreads();   // the previous tile's readers are done
+    load_rows<D>(q_lds, p.q + u.q_off, rs, qb0, u.Nq, tid);
+    load_rows<D>(do_lds, p.dout + u.q_off, rs, qb0, u.Nq, tid);
+    if (tid < kBwdTile) {
+      const int qi = qb0 + tid;
+      l_lds[tid] = qi < u.Nq ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
+      d_lds[tid] = qi < u.Nq ? p.delta[u.l_off + qi] : 0.f;
+    }
+    __syncthreads();
+    if (!wave_has || (CAUSAL && qb0 + kBwdTile - 1 < kw0)) continue;
+
+    // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys.
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int off = qb * 32 * RBP + ln.row_rd + ds * 32;
+        s[qb] = mfma32<F16>(lds16(q_lds, off), kr[ds], s[qb]);
+        dp[qb] = mfma32<F16>(lds16(do_lds, off), vr[ds], dp[qb]);
+      }
+    }
+    // P = exp2(scale log2e S - L log2e) and dS = P (dP - D), packed as B operands.
+    bf16x8 pb[2][2], dsb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 wp, wd;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {   // registers 8t + 4 half + 0..3
+          const int q4 = 32 * qb + 16 * t + 8 * half + 4 * hi;     // first of 4 queries
+          const float4 L4 = *reinterpret_cast<const float4*>(l_lds + q4);
+          const float4 D4 = *reinterpret_cast<const float4*>(d_lds + q4);
+          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 4 * half + e;
+            const bool ok = !CAUSAL || krow <= qb0 + q4 + e;
+            const float pe = ok ? __builtin_amdgcn_exp2f(s[qb][r] * p.scale_log2 - Lv[e]) : 0.f;
+            pv[e] = pe;
+            dsv[e] = pe * (dp[qb][r] - Dv[e]);
+          }
+          wp[2 * half] = pack2<F16>(pv[0], pv[1]);
+          wp[2 * half + 1] = pack2<F16>(pv[2], pv[3]);
+          wd[2 * half] = pack2<F16>(dsv[0], dsv[1]);
+          wd[2 * half + 1] = pack2<F16>(dsv[2], dsv[3]);
+        }
+        pb[qb][t] = __builtin_bit_cast(bf16x8, wp);
+        dsb[qb][t] = __builtin_bit_cast(bf16x8, wd);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r0 = (32 * qb + 16 * t) * RBP;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          dv[b] = mfma32<F16>(lds_tr8(do_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), pb[qb][t], dv[b]);
+          dk[b] = mfma32<F16>(lds_tr8(q_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), dsb[qb][t], dk[b]);
+        }
+      }
+    }
+  }
+  if (krow < u.Nk) {
+    store_rowT<D, F16>(p.dk + u.k_off + (int64_t)krow * rs, dk, p.scale, hi);
+    store_rowT<D, F16>(p.dv + u.k_off + (int64_t)krow * rs, dv, 1.f, hi);
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN, bool F16>
+__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
+                          amdgpu_waves_per_eu(1, 1)))
+void dq_kernel(BwdParams p) {
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int RBP = 2 * D + 16;
+  constexpr int TB = kBwdTile * RBP;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB];
+  uint8_t* k_lds = smem;
+  uint8_t* v_lds = smem + TB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  BwdUnit u = bwd_unit(p, VARLEN, D);
+  if (CAUSAL) u.tile = p.n_tiles - 1 - u.tile;   // longest rows first
+  const int q0 = u.tile * kBwdRows;
+  if (q0 >= u.Nq) return;
+  const int rs = (int)p.row_stride;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+
+  bf16x8 qr[DS], dor[DS];
+  float Lq = 0.f, Dq = 0.f;
+  if (qrow < u.Nq) {
+    const u32x4* qs = reinterpret_cast<const u32x4*>(p.q + u.q_off + (int64_t)qrow * rs);
+    const u32x4* os = reinterpret_cast<const u32x4*>(p.dout + u.q_off + (int64_t)qrow * rs);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qr[s] = __builtin_bit_cast(bf16x8, qs[2 * s + hi]);
+      dor[s] = __builtin_bit_cast(bf16x8, os[2 * s + hi]);
+    }
+    Lq = p.lse[u.l_off + qrow] * kLog2eF;
+    Dq = p.delta[u.l_off + qrow];
+  } else {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qr[s] = dor[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  const BwdLanes<D> ln(lane);
+  f32x16 acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+
+  const int kend = CAUSAL ? min(u.Nk, q0 + kBwdRows) : u.Nk;
+  const int n_kt = (kend + kBwdTile - 1) / kBwdTile;
+  const bool wave_has = qw0 < u.Nq;
+  const int wave_last_kt = CAUSAL ? (qw0 + 31) / kBwdTile : n_kt - 1;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int kb0 = kt * kBwdTile;
+    __syncthreads();
+    load_rows<D>(k_lds, p.k + u.k_off, rs, kb0, u.Nk, tid);
+    load_rows<D>(v_lds, p.v + u.k_off, rs, kb0, u.Nk, tid);
+    __syncthreads();
+    if (!wave_has || kt > wave_last_kt) continue;
+
+    // S^T = K Q^T and dP^T = V dO^T: this tile's 64 keys x the wave's 32 queries.
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = kb * 32 * RBP + ln.row_rd + ds * 32;
+        s[kb] = mfma32<F16>(lds16(k_lds, off), qr[ds], s[kb]);
+        dp[kb] = mfma32<F16>(lds16(v_lds, off), dor[ds], dp[kb]);
+      }
+    }
+    // dS^T = P^T (dP^T - D), packed as B operands.
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 8 * t + 2 * i + e;
+            const int key = kb0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = key < u.Nk && (!CAUSAL || key <= qrow);
+            const float pe = ok ? __builtin_amdgcn_exp2f(s[kb][r] * p.scale_log2 - Lq) : 0.f;
+            v2[e] = pe * (dp[kb][r] - Dq);
+          }
+          w[i] = pack2<F16>(v2[0], v2[1]);
+        }
+        dsb[kb][t] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r0 = (32 * kb + 16 * t) * RBP;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+          acc[b] = mfma32<F16>(lds_tr8(k_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), dsb[kb][t], acc[b]);
+      }
+    }
+  }
+  if (qrow < u.Nq) store_rowT<D, F16>(p.dq + u.q_off + (int64_t)qrow * rs, acc, p.scale, hi);
+}
+
+}  // namespace fa

@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 METRIC = "attention fwd TFLOPS (bf16) and % of MFMA peak, N=1025..8192, d=128"
+METRIC_BWD = "attention bwd TFLOPS (bf16) and % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 KERNEL_SOURCES = [os.path.join(ROOT, "aware_attention_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_api.hip")]
@@ -104,6 +105,36 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0):
             "kind": "oracle", "sample": sample + f"; float64 numpy, {dt:.1f} s"}
 
 
+def cpu_baseline_bwd(wl: dict, budget_s: float = 12.0):
+    """Time the float64 backward oracle on whole heads of the workload until budget_s is used."""
+    from oracle import attention_backward
+    threads = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        pass
+    spec = wl["spec"]
+    do = W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0]
+    per_head = 2.5 * spec.flops() / (spec.B * spec.H)
+    flops, heads, t0 = 0.0, 0, time.perf_counter()
+    for b in range(spec.B):
+        for h in range(spec.H):
+            f64 = lambda x: W.bf16_bits_to_f32(x[b, :, h]).astype(np.float64)  # noqa: E731
+            attention_backward(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), f64(do), spec.scale,
+                               spec.causal)
+            flops += per_head
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{heads} of {spec.B * spec.H} (batch, head) pairs, "
+                                        f"backward, float64 numpy, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +142,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill8k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (fa_bwd: dQ, dK, dV from a seeded dO) instead of "
+                         "the forward; FLOPs counted as 2.5x the forward's (five products)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), to "
                          "calibrate HBM byte counters against a known size")
@@ -155,7 +189,24 @@ def main():
         def step():
             aa.fa_fwd(q, k, v, softmax_scale=spec.scale, causal=spec.causal, out=o, lse=lse,
                       window=spec.window)
+
+        if args.backward:
+            if spec.window is not None:
+                print("the backward takes no window", file=sys.stderr)
+                sys.exit(2)
+            step()
+            do = to_dev(W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0])
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            delta = torch.empty_like(lse)
+            flops = 2.5 * flops
+
+            def step():  # noqa: F811 - the timed step is the backward
+                aa.fa_bwd(q, k, v, o, lse, do, softmax_scale=spec.scale, causal=spec.causal,
+                          dq=dq, dk=dk, dv=dv, delta=delta)
     else:
+        if args.backward:
+            print("--backward is measured on equal-length workloads", file=sys.stderr)
+            sys.exit(2)
         cu = torch.from_numpy(wl["cu_seqlens"]).cuda()
         total = q.shape[0]
         lse = torch.empty((spec.H, total), dtype=torch.float32, device="cuda")
@@ -184,9 +235,9 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     assert torch.isfinite(lse).all(), "non-finite log-sum-exp in the timed output"
 
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload + ("_bwd" if args.backward else ""))
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -210,8 +261,10 @@ def main():
         "kernel_digest": kernel_digest(),
         "wall_s_timed": round(wall, 4),
     }
+    if args.backward:
+        config["pass"] = "backward"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline_bwd(wl) if args.backward else cpu_baseline(wl)
     print(json.dumps(out), flush=True)
 
 

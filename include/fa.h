@@ -185,6 +185,43 @@ fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, voi
                                 int32_t causal, int32_t window_left, int32_t window_right,
                                 void* stream);
 
+/*
+ * Backward pass, equal-length batch: the gradients of O with respect to Q, K
+ * and V for an incoming gradient dO, with S and P recomputed from the saved
+ * log-sum-exp instead of stored ("FlashAttention/zh" (marovi.ai wiki),
+ * section 反向傳遞與重計算). With P_ij = exp(softmax_scale q_i.k_j - L_i):
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
+ *     dQ = softmax_scale dS K,   dK = softmax_scale dS^T Q
+ * (the chain rule through the definition; the page gives no formulas).
+ *   q, o, dout, dq : (B, Nq, H, d), dtype; dq written
+ *   k, v, dk, dv   : (B, Nk, H, d), dtype; dk, dv written
+ *   lse            : (B, H, Nq) float32, the forward's L (natural log)
+ *   delta          : (B, H, Nq) float32, caller-owned; written with D (it is
+ *                    also the backward's scratch: the library allocates none)
+ *   dtype          : FA_DTYPE_BF16 or FA_DTYPE_F16 for q, k, v, o, dout, dq,
+ *                    dk, dv; P and dS enter the matrix cores in that type
+ *   causal         : as in fa_fwd (Nq == Nk)
+ * All tensors densely packed and 16-byte aligned; o and lse are those the
+ * forward returned for the same q, k, v, scale and mask. Every element of dq,
+ * dk, dv and delta is written.
+ * Errors: as fa_fwd; an unknown dtype is FA_ERR_INVALID_ARGUMENT.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
+                 int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
+                 float softmax_scale, int32_t causal, void* stream);
+
+/*
+ * Backward pass, packed variable-length batch: tensors (total, H, d), lse
+ * and delta (H, total), cu_seqlens / num_seqs / max_seqlen / total as in
+ * fa_fwd_varlen; each sequence's gradients involve only its own rows.
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
+                        float softmax_scale, int32_t causal, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int32_t status);
 

@@ -279,3 +279,56 @@ def test_binding_accepts_f16_and_views_but_not_bad_ones():
     assert aa._strides(torch.zeros(1, 5, 1, 32)) == [0, 32, 0]
     assert aa._dtype_code(torch.float16) == _lib.FA_DTYPE_F16
     assert aa._dtype_code(torch.bfloat16) == _lib.FA_DTYPE_BF16
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, delta=P, B=1, Nq=128, Nk=128, H=2,
+             d=64, dtype=_lib.FA_DTYPE_BF16, scale=0.125, causal=0, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                           a["dv"], a["delta"], a["B"], a["Nq"], a["Nk"], a["H"], a["d"],
+                           a["dtype"], a["scale"], a["causal"], a["stream"])
+
+
+def _bwd_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, delta=P, cu=P, num_seqs=2,
+             max_seqlen=100, total=150, H=2, d=128, dtype=_lib.FA_DTYPE_F16, scale=0.1, causal=1,
+             stream=None)
+    a.update(kw)
+    return _lib.raw_fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                  a["dk"], a["dv"], a["delta"], a["cu"], a["num_seqs"],
+                                  a["max_seqlen"], a["total"], a["H"], a["d"], a["dtype"],
+                                  a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(do=None), INV), (dict(lse=None), INV), (dict(delta=None), INV),
+    (dict(dq=None), INV), (dict(dv=P + 8), INV), (dict(delta=P + 4), INV),
+    (dict(B=0), INV), (dict(Nk=0), INV), (dict(H=0), INV), (dict(causal=2), INV),
+    (dict(causal=1, Nk=64), INV), (dict(dtype=3), INV), (dict(scale=float("nan")), INV),
+    (dict(d=48), UNS), (dict(scale=-1.0), UNS),
+])
+def test_fa_bwd_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _bwd(**kw) == code
+    assert _lib.load().fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), INV), (dict(num_seqs=0), INV), (dict(max_seqlen=200), INV),
+    (dict(dk=None), INV), (dict(dtype=-1), INV), (dict(d=16), UNS),
+])
+def test_fa_bwd_varlen_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _bwd_varlen(**kw) == code
+
+
+def test_bwd_valid_calls_without_a_device_are_hip_errors():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _bwd() == HIP
+    assert _bwd(causal=1, dtype=_lib.FA_DTYPE_F16) == HIP
+    assert _bwd_varlen() == HIP
+    assert _bwd_varlen(total=0, max_seqlen=0) == _lib.FA_OK

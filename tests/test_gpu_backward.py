@@ -1,0 +1,257 @@
+"""Backward (fa_bwd / fa_bwd_varlen): HIP path vs the float64 CPU oracle.
+
+The kernels receive O and L computed by the oracle's forward (O rounded to
+the input type, L to fp32), so these tests check the backward alone; one
+test chains the HIP forward into the HIP backward.
+
+Tolerance (no figure on the pages): a gradient row (one token, one head,
+d values) is a sum of products of 16-bit P or dS with 16-bit dO, Q or K,
+accumulated in fp32 and rounded to 16 bits once. The rounding of P and dS
+(2^-9 relative for bf16) dominates, and its sum stays within a few 2^-9 of
+that row's own RMS. Rows differ in scale by an order of magnitude: a causal
+row that sees only a few keys has dS values of several units, and its dQ
+row (and the dK rows of the keys it sees) are far above the tensor's RMS.
+The bar is |gpu - ref| <= 2e-2 (rms_row(ref) + |ref|) + 1e-3 rms(ref) per
+element (about ten times the expected error; the middle term covers rows
+that are exactly zero, such as dQ of a row with one visible key).
+
+One more term, derived rather than tuned: the method forms D_i = dO_i . O_i
+from the 16-bit O the forward returned, not from the exact O (the identity
+D_i = sum_j P_ij dP_ij holds only for the exact one). Rounding O by a
+relative eps moves D_i by at most dD_i = eps sum_e |dO_ie O_ie|, which moves
+dS_ij by P_ij dD_i with the same sign across the row, so it does not cancel:
+it adds up to scale dD_i sum_j P_ij |K_je| to dQ and scale sum_i P_ij dD_i
+|Q_ie| to dK (dV does not depend on D). eps is 2^-8 for bf16 and 2^-10 for
+fp16 (twice the unit roundoff), and 2^-6 where O comes from the HIP forward
+(its own P and output rounding). D itself is one value per row:
+|gpu - ref| <= 2e-2 (rms(ref) + |ref|) + dD.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import (attention_backward_dense, attention_backward_varlen, attention_dense,
+                    attention_probs, attention_varlen)
+from tests.gpu_util import say, to_dev, to_f64, torch_or_skip
+
+pytestmark = pytest.mark.gpu
+G_TOL = 2e-2
+EPS_O = {"bf16": 2.0**-8, "f16": 2.0**-10}   # relative rounding of O, doubled
+EPS_O_HIP = 2.0**-6                          # O from the HIP forward
+
+
+def d_rounding_terms(qf, kf, vf, dof, scale, causal, eps):
+    """One head: the dq, dk and D bounds of the D-from-16-bit-O rounding (module docstring)."""
+    P = attention_probs(qf, kf, scale, causal)
+    O = P @ vf
+    dD = eps * np.sum(np.abs(dof * O), axis=1)                       # (Nq,)
+    tq = scale * dD[:, None] * (P @ np.abs(kf))                      # (Nq, d)
+    tk = scale * (P.T @ (dD[:, None] * np.abs(qf)))                  # (Nk, d)
+    return tq, tk, dD
+
+
+def dense_terms(qf, kf, vf, dof, scale, causal, eps):
+    """d_rounding_terms over (B, N, H, d) tensors: tq, tk in the tensors' layouts, dD (B, H, Nq)."""
+    B, Nq, H, _ = qf.shape
+    tq, tk = np.zeros_like(qf), np.zeros_like(kf)
+    dD = np.zeros((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            tq[b, :, h], tk[b, :, h], dD[b, h] = d_rounding_terms(
+                qf[b, :, h], kf[b, :, h], vf[b, :, h], dof[b, :, h], scale, causal, eps)
+    return tq, tk, dD
+
+
+def assert_grad_close(got, ref, what, per_row=True, extra=0.0):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    if per_row:
+        row_rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+        bound = G_TOL * (row_rms + np.abs(ref)) + 1e-3 * rms
+    else:
+        bound = G_TOL * (rms + np.abs(ref))
+    bad = err > bound + extra
+    if bad.any():
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance, first {idx}: "
+                             f"gpu {got[idx]} ref {ref[idx]} (rms {rms:.3e}, max err {err.max():.3e})")
+
+
+def _round(x64, dtype):
+    """float64 values -> 16-bit patterns of dtype."""
+    x = np.asarray(x64, dtype=np.float32)
+    return W.f32_to_bf16_bits(x) if dtype == "bf16" else W.f32_to_f16_bits(x)
+
+
+def _np(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def check_bwd_dense(B, Nq, Nk, H, d, causal, seed, dtype="bf16"):
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    say(f"bwd dense B={B} Nq={Nq} Nk={Nk} H={H} d={d} causal={causal} dtype={dtype} seed={seed}")
+    q, k, v = W.make_dense(B, Nq, H, d, seed, Nk=Nk, dtype=dtype)
+    do, _, _ = W.make_dense(B, Nq, H, d, seed + 1, dtype=dtype)
+    scale = 1 / np.sqrt(d)
+    qf, kf, vf, dof = (to_f64(x, dtype) for x in (q, k, v, do))
+    oref, lref = attention_dense(qf, kf, vf, scale, causal)
+    dq, dk, dv, delta = aa.fa_bwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                  to_dev(_round(oref, dtype), dtype),
+                                  torch.from_numpy(lref.astype(np.float32)).cuda(),
+                                  to_dev(do, dtype), softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    gq, gk, gv, gd = attention_backward_dense(qf, kf, vf, dof, scale, causal)
+    tq, tk, dD = dense_terms(qf, kf, vf, dof, scale, causal, EPS_O[dtype])
+    what = f"Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype}"
+    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
+    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
+    assert_grad_close(_np(dv), gv, "dv " + what)
+    assert_grad_close(_np(delta), gd, "delta " + what, per_row=False, extra=dD)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 200])
+def test_bwd_dense(d, causal, N):
+    check_bwd_dense(2, N, N, 2, d, causal, seed=8000 + N + d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nq,Nk", [(129, 300), (300, 129), (1, 77)])
+def test_bwd_cross_lengths(d, Nq, Nk):
+    check_bwd_dense(1, Nq, Nk, 2, d, False, seed=8100 + Nq + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_long_rows(causal):
+    # 6 key tiles of 128 rows for dK/dV, 6 query tiles for dQ, 64-row streamed tiles.
+    check_bwd_dense(1, 700, 700, 2, 128, causal, seed=8200)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f16(d, causal):
+    check_bwd_dense(2, 333, 333, 2, d, causal, seed=8300 + d, dtype="f16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen(causal):
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    lengths = [1, 127, 0, 200, 64, 300]
+    H, d = 2, 64
+    say(f"bwd varlen lengths={lengths} causal={causal}")
+    q, k, v, cu = W.make_varlen(lengths, H, d, seed=8400)
+    do, _, _, _ = W.make_varlen(lengths, H, d, seed=8401)
+    scale = 1 / np.sqrt(d)
+    qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
+    oref, lref = attention_varlen(qf, kf, vf, cu, scale, causal)
+    dq, dk, dv, delta = aa.fa_bwd_varlen(to_dev(q), to_dev(k), to_dev(v), to_dev(_round(oref, "bf16")),
+                                         torch.from_numpy(lref.astype(np.float32)).cuda(), to_dev(do),
+                                         torch.from_numpy(cu).cuda(), max(lengths),
+                                         softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    gq, gk, gv, gd = attention_backward_varlen(qf, kf, vf, dof, cu, scale, causal)
+    tq, tk, dD = np.zeros_like(qf), np.zeros_like(kf), np.zeros((H, qf.shape[0]))
+    for s_ in range(len(lengths)):
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        for h in range(H):
+            if b > a:
+                tq[a:b, h], tk[a:b, h], dD[h, a:b] = d_rounding_terms(
+                    qf[a:b, h], kf[a:b, h], vf[a:b, h], dof[a:b, h], scale, causal, EPS_O["bf16"])
+    assert_grad_close(_np(dq), gq, f"varlen dq causal={causal}", extra=tq)
+    assert_grad_close(_np(dk), gk, f"varlen dk causal={causal}", extra=tk)
+    assert_grad_close(_np(dv), gv, f"varlen dv causal={causal}")
+    assert_grad_close(_np(delta), gd, f"varlen delta causal={causal}", per_row=False, extra=dD)
+
+
+def test_bwd_single_key_closed_form():
+    """One key: P = 1, so dq = dk = 0 and dv = the sum of dO over the queries."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    say("bwd single key")
+    q, k, v = (to_dev(x) for x in W.make_dense(1, 300, 2, 64, seed=8500, Nk=1))
+    do = to_dev(W.make_dense(1, 300, 2, 64, seed=8501)[0])
+    o, lse = aa.fa_fwd(q, k, v)
+    dq, dk, dv, _ = aa.fa_bwd(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    # dS = P (dP - D) is 0 up to D: here O = v0 exactly (one key), so dP and D are
+    # two fp32 sums of the same 64 products
+    assert float(dq.abs().max()) <= 1e-3 and float(dk.abs().max()) <= 1e-3
+    want = do.double().sum(dim=1, keepdim=True)
+    assert_grad_close(_np(dv), want.cpu().numpy(), "dv = sum of dO")
+
+
+def test_bwd_chained_with_forward_and_autograd():
+    """HIP forward -> HIP backward against the oracle, and the autograd wrapper
+    gives the same gradients bit for bit."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    B, N, H, d = 2, 400, 2, 128
+    say("bwd chained with the HIP forward, autograd wrapper")
+    q, k, v = W.make_dense(B, N, H, d, seed=8600)
+    do = W.make_dense(B, N, H, d, seed=8601)[0]
+    qd, kd, vd, dod = (to_dev(x) for x in (q, k, v, do))
+    o, lse = aa.fa_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv, _ = aa.fa_bwd(qd, kd, vd, o, lse, dod, causal=True)
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (qd, kd, vd))
+    oa = aa.attention(qa, ka, va, causal=True)
+    oa.backward(dod)
+    torch.cuda.synchronize()
+    for a, b, n in ((qa.grad, dq, "dq"), (ka.grad, dk, "dk"), (va.grad, dv, "dv")):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+    f = [to_f64(x) for x in (q, k, v, do)]
+    gq, gk, gv, _ = attention_backward_dense(*f, 1 / np.sqrt(d), True)
+    tq, tk, _ = dense_terms(*f, 1 / np.sqrt(d), True, EPS_O_HIP)
+    assert_grad_close(_np(dq), gq, "chained dq", extra=tq)
+    assert_grad_close(_np(dk), gk, "chained dk", extra=tk)
+    assert_grad_close(_np(dv), gv, "chained dv")
+
+
+def test_bwd_deterministic():
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    say("bwd determinism")
+    q, k, v = (to_dev(x) for x in W.make_dense(1, 600, 4, 64, seed=8700))
+    do = to_dev(W.make_dense(1, 600, 4, 64, seed=8701)[0])
+    o, lse = aa.fa_fwd(q, k, v)
+    g1 = aa.fa_bwd(q, k, v, o, lse, do)
+    g2 = aa.fa_bwd(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    for a, b in zip(g1[:3], g2[:3]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(g1[3], g2[3])
+
+
+def test_bwd_full_size_prefill_sampled():
+    """prefill2k's shape (B=4, H=32, N=2048, d=128, causal): whole (batch, head)
+    pairs against the oracle, and at every head the key-shift invariant: the dK
+    rows sum to zero (relative to their scale)."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    w = W.WORKLOADS["prefill2k"]
+    say(f"bwd full-size prefill2k B={w.B} N={w.N} H={w.H}")
+    q, k, v = W.make_dense(w.B, w.N, w.H, w.d, w.seed)
+    do = W.make_dense(w.B, w.N, w.H, w.d, w.seed + 1)[0]
+    qd, kd, vd, dod = (to_dev(x) for x in (q, k, v, do))
+    o, lse = aa.fa_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv, delta = aa.fa_bwd(qd, kd, vd, o, lse, dod, causal=True)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (2, 13)]:
+        sl = lambda x: to_f64(x[b:b + 1, :, h:h + 1])  # noqa: E731
+        gq, gk, gv, _ = attention_backward_dense(sl(q), sl(k), sl(v), sl(do), w.scale, True)
+        tq, tk, _ = dense_terms(sl(q), sl(k), sl(v), sl(do), w.scale, True, EPS_O_HIP)
+        assert_grad_close(_np(dq[b:b + 1, :, h:h + 1]), gq, f"prefill2k dq b={b} h={h}", extra=tq)
+        assert_grad_close(_np(dk[b:b + 1, :, h:h + 1]), gk, f"prefill2k dk b={b} h={h}", extra=tk)
+        assert_grad_close(_np(dv[b:b + 1, :, h:h + 1]), gv, f"prefill2k dv b={b} h={h}")
+    dkf = dk.double()
+    colsum = dkf.sum(dim=1).abs()                            # (B, H, d)
+    scale_ = dkf.abs().sum(dim=1)
+    assert torch.isfinite(dkf).all() and torch.isfinite(dq.double()).all()
+    assert bool((colsum <= 2e-2 * scale_ + 1e-3).all()), float((colsum / scale_).max())
