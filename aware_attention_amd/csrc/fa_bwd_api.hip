@@ -57,6 +57,8 @@ hipError_t launch_bwd(const fa::BwdParams& p, int d, int32_t dtype, bool causal,
 
 fa_status check_bwd_common(int32_t H, int32_t d, int32_t dtype, float scale, int32_t causal) {
   if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
+  // The tile copies address a 64-row tile with 32-bit byte offsets.
+  if ((int64_t)H * d > (int64_t{1} << 24)) return fail(FA_ERR_UNSUPPORTED, "H * d above 2^24");
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");

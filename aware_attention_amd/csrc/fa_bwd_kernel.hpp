@@ -101,19 +101,28 @@ void delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ d
   delta[(bidx * H + head) * N + n] = acc;
 }
 
-// Row-major LDS tile of kBwdTile rows, rows padded to 2 D + 16 bytes; rows
-// at or past nvalid are zero.
+// Row-major LDS tile of kBwdTile rows, each padded to 2 D + 16 bytes, i.e.
+// SL = D/8 + 1 slots of 16 bytes (slot D/8 of a row is padding). The tile's
+// kBwdTile * SL slots are exactly SL blocks of 64 slots, so it is filled by
+// SL direct HBM -> LDS copies of 64 lanes (global_load_lds_dwordx4), split
+// over the workgroup's waves: lane l of copy i fills slot 64 i + l. Rows at
+// or past nvalid are filled with the last valid row: the kernels give them
+// P = 0, so they contribute nothing, and no read leaves the tensor. The
+// copies are asynchronous; the issuing wave waits for them (s_waitcnt)
+// before the barrier that publishes the tile.
 template <int D>
-__device__ __forceinline__ void load_rows(uint8_t* lds, const uint16_t* g, int64_t rs, int row0,
-                                          int nvalid, int tid) {
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int RBP = 2 * D + 16;
+__device__ __forceinline__ void copy_tile_async(uint32_t lds_tile, const uint16_t* g, int rs,
+                                                int row0, int nvalid, int wave, int lane) {
+  constexpr int SL = D / 8 + 1;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(g + (int64_t)row0 * rs);
+  const int last = nvalid - 1 - row0;        // last valid row of the tile, >= 0
 #pragma unroll
-  for (int c = tid; c < kBwdTile * CH; c += kBwdThreads) {
-    const int r = c / CH, ch = c % CH;
-    u32x4 val = {0, 0, 0, 0};
-    if (row0 + r < nvalid) val = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * rs + ch * 8);
-    *reinterpret_cast<u32x4*>(lds + r * RBP + ch * 16) = val;
+  for (int i = wave; i < SL; i += kBwdWaves) {
+    const int slot = 64 * i + lane;
+    const int row = slot / SL, ch = slot % SL;
+    const int r = row < last ? row : last;
+    const int c = ch < D / 8 ? ch : 0;        // the padding slot re-reads chunk 0
+    copy16_to_lds(base, (uint32_t)(r * 2 * rs + 16 * c), lds_tile + 1024 * i);
   }
 }
 
@@ -198,11 +207,10 @@ void dkdv_kernel(BwdParams p) {
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = kBwdTile * RBP;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB + 2 * kBwdTile * 4];
-  uint8_t* q_lds = smem;
-  uint8_t* do_lds = smem + TB;
-  float* l_lds = reinterpret_cast<float*>(smem + 2 * TB);   // L * log2(e) per query
-  float* d_lds = l_lds + kBwdTile;                          // D per query
+  // [Q 0][dO 0][Q 1][dO 1][L 0][D 0][L 1][D 1]: buffer b holds query tile
+  // qt0 + 2 m + b; L (times log2 e) and D per query of the tile.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB + 4 * kBwdTile * 4];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   // Causal: key tiles in ascending order see the most queries first.
@@ -234,18 +242,47 @@ void dkdv_kernel(BwdParams p) {
   const int n_qt = (u.Nq + kBwdTile - 1) / kBwdTile;
   const int qt0 = CAUSAL ? k0 / kBwdTile : 0;
   const bool wave_has = kw0 < u.Nk;
+  // Copies of query tile qt into buffer b, and its L, D values into registers
+  // (threads 0..63, one query each; padding queries get L = +inf, D = 0).
+  auto issue = [&](int qt, int b) __attribute__((always_inline)) {
+    copy_tile_async<D>(smem_lds + (2 * b) * TB, p.q + u.q_off, rs, qt * kBwdTile, u.Nq, wave, lane);
+    copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.dout + u.q_off, rs, qt * kBwdTile, u.Nq, wave,
+                       lane);
+  };
+  auto load_ld = [&](int qt, float& lv, float& dv_) __attribute__((always_inline)) {
+    const int qi = qt * kBwdTile + tid;
+    lv = qi < u.Nq ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
+    dv_ = qi < u.Nq ? p.delta[u.l_off + qi] : 0.f;
+  };
+  auto store_ld = [&](int b, float lv, float dv_) __attribute__((always_inline)) {
+    float* ld = reinterpret_cast<float*>(smem + 4 * TB) + b * 2 * kBwdTile;
+    ld[tid] = lv;
+    ld[kBwdTile + tid] = dv_;
+  };
+  if (qt0 < n_qt) {
+    issue(qt0, 0);
+    if (tid < kBwdTile) {
+      float lv, dv_;
+      load_ld(qt0, lv, dv_);
+      store_ld(0, lv, dv_);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int qt = qt0; qt < n_qt; ++qt) {
     const int qb0 = qt * kBwdTile;
-    __syncthreads();   // the previous tile's readers are done
-    load_rows<D>(q_lds, p.q + u.q_off, rs, qb0, u.Nq, tid);
-    load_rows<D>(do_lds, p.dout + u.q_off, rs, qb0, u.Nq, tid);
-    if (tid < kBwdTile) {
-      const int qi = qb0 + tid;
-      l_lds[tid] = qi < u.Nq ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
-      d_lds[tid] = qi < u.Nq ? p.delta[u.l_off + qi] : 0.f;
+    const int buf = (qt - qt0) & 1;
+    const bool more = qt + 1 < n_qt;
+    float nl = 0.f, nd = 0.f;
+    if (more) {   // the other buffer was last read before the previous barrier
+      issue(qt + 1, buf ^ 1);
+      if (tid < kBwdTile) load_ld(qt + 1, nl, nd);
     }
-    __syncthreads();
-    if (!wave_has || (CAUSAL && qb0 + kBwdTile - 1 < kw0)) continue;
+    const uint8_t* q_lds = smem + (2 * buf) * TB;
+    const uint8_t* do_lds = smem + (2 * buf + 1) * TB;
+    const float* l_lds = reinterpret_cast<const float*>(smem + 4 * TB) + buf * 2 * kBwdTile;
+    const float* d_lds = l_lds + kBwdTile;
+    if (wave_has && !(CAUSAL && qb0 + kBwdTile - 1 < kw0)) {
 
     // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys.
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -302,6 +339,10 @@ void dkdv_kernel(BwdParams p) {
         }
       }
     }
+    }
+    if (more && tid < kBwdTile) store_ld(buf ^ 1, nl, nd);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
+    __syncthreads();
   }
   if (krow < u.Nk) {
     store_rowT<D, F16>(p.dk + u.k_off + (int64_t)krow * rs, dk, p.scale, hi);
@@ -316,9 +357,9 @@ void dq_kernel(BwdParams p) {
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = kBwdTile * RBP;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB];
-  uint8_t* k_lds = smem;
-  uint8_t* v_lds = smem + TB;
+  // [K 0][V 0][K 1][V 1]: buffer b holds key tile 2 m + b.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   BwdUnit u = bwd_unit(p, VARLEN, D);
@@ -354,13 +395,21 @@ void dq_kernel(BwdParams p) {
   const int n_kt = (kend + kBwdTile - 1) / kBwdTile;
   const bool wave_has = qw0 < u.Nq;
   const int wave_last_kt = CAUSAL ? (qw0 + 31) / kBwdTile : n_kt - 1;
+  auto issue = [&](int kt, int b) __attribute__((always_inline)) {
+    copy_tile_async<D>(smem_lds + (2 * b) * TB, p.k + u.k_off, rs, kt * kBwdTile, u.Nk, wave, lane);
+    copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.v + u.k_off, rs, kt * kBwdTile, u.Nk, wave,
+                       lane);
+  };
+  if (n_kt > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int kb0 = kt * kBwdTile;
-    __syncthreads();
-    load_rows<D>(k_lds, p.k + u.k_off, rs, kb0, u.Nk, tid);
-    load_rows<D>(v_lds, p.v + u.k_off, rs, kb0, u.Nk, tid);
-    __syncthreads();
-    if (!wave_has || kt > wave_last_kt) continue;
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);   // buffer last read before the previous barrier
+    const uint8_t* k_lds = smem + (2 * buf) * TB;
+    const uint8_t* v_lds = smem + (2 * buf + 1) * TB;
+    if (wave_has && kt <= wave_last_kt) {
 
     // S^T = K Q^T and dP^T = V dO^T: this tile's 64 keys x the wave's 32 queries.
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -407,6 +456,9 @@ void dq_kernel(BwdParams p) {
           acc[b] = mfma32<F16>(lds_tr8(k_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), dsb[kb][t], acc[b]);
       }
     }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
+    __syncthreads();
   }
   if (qrow < u.Nq) store_rowT<D, F16>(p.dq + u.q_off + (int64_t)qrow * rs, acc, p.scale, hi);
 }

@@ -204,7 +204,8 @@ fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, voi
  * All tensors densely packed and 16-byte aligned; o and lse are those the
  * forward returned for the same q, k, v, scale and mask. Every element of dq,
  * dk, dv and delta is written.
- * Errors: as fa_fwd; an unknown dtype is FA_ERR_INVALID_ARGUMENT.
+ * Errors: as fa_fwd; an unknown dtype is FA_ERR_INVALID_ARGUMENT; H * d above
+ * 2^24 is FA_ERR_UNSUPPORTED.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
