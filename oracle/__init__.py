@@ -13,13 +13,16 @@ Contents:
                 it out, in float64, used only to cross-check the definition.
   backward.py   the gradients dQ, dK, dV of the definition (chain rule through
                 the softmax), with P materialised, in float64.
+  padding.py    attention over a padded batch with a key padding mask: remove
+                the padding, attend, put the result back (zeros at padding).
 """
 from .attention import (attention, attention_probs, attention_dense,
                         attention_varlen, ORACLE_DTYPE)
 from .backward import (attention_backward, attention_backward_dense,
                        attention_backward_varlen)
+from .padding import attention_padded
 from .tiled import attention_tiled
 
 __all__ = ["attention", "attention_probs", "attention_dense", "attention_varlen",
            "attention_tiled", "attention_backward", "attention_backward_dense",
-           "attention_backward_varlen", "ORACLE_DTYPE"]
+           "attention_backward_varlen", "attention_padded", "ORACLE_DTYPE"]

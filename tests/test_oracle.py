@@ -161,3 +161,89 @@ def test_backward_wrappers_match_single_head():
     g = attention_backward(qv[3:8, 1], kv[3:8, 1], vv[3:8, 1], dov[3:8, 1], 0.5, False)
     np.testing.assert_array_equal(dk[3:8, 1], g[1])
     np.testing.assert_array_equal(delta[1, 3:8], g[3])
+
+
+# ---------------------------------------------------------------------------
+# Key padding mask (remove the padding, attend, put back)
+# ---------------------------------------------------------------------------
+
+from oracle import attention_padded  # noqa: E402
+from tests.oracle_pins import _close, _close_inf, brute_force  # noqa: E402
+
+
+def _brute_force_masked(q, k, v, valid, scale, causal):
+    """Pure Python: scores of padding keys (and, when causal, of later keys) left
+    out of the sums in the padded positions, no removal of rows; padding rows
+    give 0 and -inf."""
+    N = len(q)
+    O, L = [], []
+    for i in range(N):
+        if not valid[i]:
+            O.append([0.0] * len(v[0]))
+            L.append(-math.inf)
+            continue
+        w = [(math.exp(scale * math.fsum(a * b for a, b in zip(q[i], k[j]))), j)
+             for j in range(N) if valid[j] and (not causal or j <= i)]
+        Z = math.fsum(e for e, _ in w)
+        O.append([math.fsum(e * v[j][c] for e, j in w) / Z for c in range(len(v[0]))])
+        L.append(math.log(Z))
+    return O, L
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_matches_masked_brute_force(causal):
+    rng = np.random.default_rng(41)
+    B, S, H, d = 3, 7, 2, 3
+    q, k, v = (rng.standard_normal((B, S, H, d)) for _ in range(3))
+    mask = np.array([[1, 1, 1, 1, 0, 0, 0], [0, 1, 0, 1, 1, 0, 1], [0] * 7], dtype=np.uint8)
+    O, L = attention_padded(q, k, v, mask, 0.8, causal)
+    for b in range(B):
+        for h in range(H):
+            Ob, Lb = _brute_force_masked(q[b, :, h].tolist(), k[b, :, h].tolist(),
+                                         v[b, :, h].tolist(), mask[b].tolist(), 0.8, causal)
+            _close(O[b, :, h], Ob, 1e-12, f"padded O b={b} h={h}")
+            _close_inf(L[b, h], Lb, 1e-12, f"padded L b={b} h={h}")
+
+
+def test_padded_all_valid_is_plain_attention():
+    rng = np.random.default_rng(42)
+    q, k, v = (rng.standard_normal((2, 9, 3, 4)) for _ in range(3))
+    for causal in (False, True):
+        O, L = attention_padded(q, k, v, np.ones((2, 9), dtype=np.uint8), 0.6, causal)
+        Od, Ld = attention_dense(q, k, v, 0.6, causal)
+        np.testing.assert_array_equal(O, Od)
+        np.testing.assert_array_equal(L, Ld)
+
+
+def test_padded_right_padding_is_varlen():
+    """Right padding (first n_b tokens valid) is the packed varlen batch of those lengths."""
+    rng = np.random.default_rng(43)
+    B, S, H, d = 3, 8, 2, 4
+    lengths = [8, 3, 5]
+    q, k, v = (rng.standard_normal((B, S, H, d)) for _ in range(3))
+    mask = np.array([[1] * n + [0] * (S - n) for n in lengths], dtype=np.uint8)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    pack = lambda x: np.concatenate([x[b, :n] for b, n in enumerate(lengths)])  # noqa: E731
+    for causal in (False, True):
+        O, L = attention_padded(q, k, v, mask, 0.5, causal)
+        Ov, Lv = attention_varlen(pack(q), pack(k), pack(v), cu, 0.5, causal)
+        for b, n in enumerate(lengths):
+            a = int(cu[b])
+            _close(O[b, :n], Ov[a:a + n], 1e-13, "right padding O")
+            _close(L[b, :, :n], Lv[:, a:a + n], 1e-13, "right padding L")
+            assert np.all(O[b, n:] == 0) and np.all(np.isneginf(L[b, :, n:]))
+
+
+def test_padded_keys_ignore_padding_content():
+    """Changing q, k, v at padding positions changes nothing (non-causal and causal)."""
+    rng = np.random.default_rng(44)
+    q, k, v = (rng.standard_normal((1, 10, 1, 4)) for _ in range(3))
+    mask = np.array([[1, 0, 1, 1, 0, 1, 1, 1, 0, 1]], dtype=np.uint8)
+    for causal in (False, True):
+        O1, L1 = attention_padded(q, k, v, mask, 0.7, causal)
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        for x in (q2, k2, v2):
+            x[0, mask[0] == 0] = 50.0
+        O2, L2 = attention_padded(q2, k2, v2, mask, 0.7, causal)
+        np.testing.assert_array_equal(O1, O2)
+        np.testing.assert_array_equal(L1, L2)

@@ -217,3 +217,62 @@ def test_bwd_mutant_is_caught(mutation):
         except Exception:  # noqa: BLE001 - any failure counts as caught
             failed.append(pin.__name__)
     assert failed, f"backward mutation {mutation!r} passed every backward pin"
+
+
+# ---------------------------------------------------------------------------
+# Key padding mask: planted mistakes in a copy of the padded route must each
+# fail the padded pins of test_oracle.py.
+# ---------------------------------------------------------------------------
+
+from oracle import attention  # noqa: E402
+
+PAD_MUTATIONS = ["mask_inverted", "padding_rows_not_zeroed", "padding_l_zero",
+                 "padding_keys_kept", "causal_over_compacted_reversed"]
+
+
+def _make_padded(mutation):
+    def fn(q, k, v, mask, scale, causal):
+        B, S, H, _ = q.shape
+        m = np.asarray(mask) != 0
+        if mutation == "mask_inverted":
+            m = ~m
+        O = np.zeros((B, S, H, v.shape[3])) if mutation != "padding_rows_not_zeroed" \
+            else np.ones((B, S, H, v.shape[3]))
+        L = np.full((B, H, S), 0.0 if mutation == "padding_l_zero" else -np.inf)
+        for b in range(B):
+            idx = np.arange(S) if mutation == "padding_keys_kept" else np.nonzero(m[b])[0]
+            if idx.size == 0:
+                continue
+            if mutation == "causal_over_compacted_reversed":
+                idx = idx[::-1]
+            for h in range(H):
+                o, lse = attention(q[b, idx, h], k[b, idx, h], v[b, idx, h], scale, causal)
+                rows = idx if mutation != "padding_keys_kept" else np.nonzero(m[b])[0]
+                sel = slice(None) if mutation != "padding_keys_kept" else rows
+                O[b, rows, h] = o[sel]
+                L[b, h, rows] = lse[sel]
+        return O, L
+    return fn
+
+
+def _padded_pins(fn):
+    import tests.test_oracle as T
+    orig = T.attention_padded
+    T.attention_padded = fn
+    try:
+        T.test_padded_matches_masked_brute_force(False)
+        T.test_padded_matches_masked_brute_force(True)
+        T.test_padded_all_valid_is_plain_attention()
+        T.test_padded_right_padding_is_varlen()
+    finally:
+        T.attention_padded = orig
+
+
+def test_padded_reference_copy_passes():
+    _padded_pins(_make_padded("none"))
+
+
+@pytest.mark.parametrize("mutation", PAD_MUTATIONS)
+def test_padded_mutant_is_caught(mutation):
+    with pytest.raises(Exception):  # noqa: B017 - any failure counts as caught
+        _padded_pins(_make_padded(mutation))
