@@ -39,7 +39,8 @@ import math
 
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
                    FA_ERR_UNSUPPORTED, FA_OK, FaError, check, load, raw_fa_bwd, raw_fa_bwd_varlen,
-                   raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_strided, raw_fa_fwd_varlen,
+                   raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
+                   raw_fa_fwd_varlen,
                    raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "attention", "FaError", "load",
@@ -110,8 +111,13 @@ def _window(window, causal):
     return tuple(min(w, 2**31 - 1) for w in sides)
 
 
-def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, window=None):
-    """Attention forward over an equal-length batch; returns (o, lse)."""
+def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, window=None,
+           key_padding_mask=None):
+    """Attention forward over an equal-length batch; returns (o, lse).
+
+    key_padding_mask (B, S) bool or uint8 on q's device, nonzero = valid token:
+    self-attention over the valid tokens of each batch row, padding positions
+    returning o = 0 and lse = -inf (fa_fwd_padded)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check_tensor(t, n, 4)
@@ -131,6 +137,24 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, window
     scale = _scale(softmax_scale, d)
     wl, wr = (-1, -1) if window is None else _window(window, causal)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if key_padding_mask is not None:
+        m = key_padding_mask
+        if window is not None:
+            raise ValueError("key_padding_mask and window are exclusive")
+        if Nk != Nq:
+            raise ValueError("key_padding_mask is for self-attention (Nq == Nk)")
+        if not all(t.is_contiguous() for t in (q, k, v, out)):
+            raise ValueError("q, k, v and out must be contiguous with key_padding_mask")
+        if not isinstance(m, torch.Tensor) or m.dtype not in (torch.bool, torch.uint8) \
+                or tuple(m.shape) != (B, Nq) or m.device != q.device or not m.is_contiguous():
+            raise ValueError("key_padding_mask must be a contiguous (B, S) bool or uint8 tensor "
+                             "on q's device")
+        m = m.view(torch.uint8)
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            check(raw_fa_fwd_padded(*ptrs, m.data_ptr(), B, Nq, H, d, _dtype_code(q.dtype), scale,
+                                    int(bool(causal)), stream))
+        return out, lse
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         if not _plain(q, k, v, out):

@@ -18,7 +18,7 @@ FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
-            "fa_fwd_varlen_strided", "fa_bwd", "fa_bwd_varlen", "fa_status_string",
+            "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_status_string",
             "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen_strided.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, p64, p64,
                                           p64, p64, i32, f32, i32, i32, i32, vp]
     lib.fa_fwd_varlen_strided.restype = i32
+    lib.fa_fwd_padded.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_padded.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_bwd_varlen.argtypes = [vp] * 11 + [i32, i32, i32, i32, i32, i32, f32, i32, vp]
@@ -142,3 +144,8 @@ def raw_fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs, ma
     """Pointer-level call of fa_bwd_varlen; returns the status code."""
     return load().fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs,
                                 max_seqlen, total, H, d, dtype, scale, causal, stream)
+
+
+def raw_fa_fwd_padded(q, k, v, o, lse, mask, B, S, H, d, dtype, scale, causal, stream) -> int:
+    """Pointer-level call of fa_fwd_padded; returns the status code."""
+    return load().fa_fwd_padded(q, k, v, o, lse, mask, B, S, H, d, dtype, scale, causal, stream)

@@ -63,21 +63,29 @@ using fa_host::check_device;
 using fa_host::fail;
 using fa_host::g_last_error;
 
-template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16>
+template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16, bool KPM = false>
 hipError_t launch_one(const fa::FwdParams& p, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN, BAND, F16>), dim3(grid),
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, VARLEN, BAND, F16, KPM>), dim3(grid),
                      dim3(fa::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-// Mask of a launch: none, causal (top-left, Nq == Nk) or a band.
-enum class Mask { kNone, kCausal, kBand };
+// Mask of a launch: none, causal (top-left, Nq == Nk), a band, or a key
+// padding mask (dense self-attention), alone or with causal.
+enum class Mask { kNone, kCausal, kBand, kPad, kPadCausal };
 
 template <int D, bool VARLEN, bool F16>
 hipError_t launch_d(const fa::FwdParams& p, Mask mask, uint32_t grid, hipStream_t stream) {
   switch (mask) {
     case Mask::kCausal: return launch_one<D, true, VARLEN, false, F16>(p, grid, stream);
     case Mask::kBand: return launch_one<D, false, VARLEN, true, F16>(p, grid, stream);
+    case Mask::kPad:
+    case Mask::kPadCausal:
+      if constexpr (!VARLEN) {
+        return mask == Mask::kPad ? launch_one<D, false, false, false, F16, true>(p, grid, stream)
+                                  : launch_one<D, true, false, false, F16, true>(p, grid, stream);
+      }
+      return hipErrorInvalidValue;
     default: return launch_one<D, false, VARLEN, false, F16>(p, grid, stream);
   }
 }
@@ -175,7 +183,8 @@ const char* const kTensorNames[4] = {"q", "k", "v", "o"};
 fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                     int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
                     const Strides st[4], int32_t dtype, float softmax_scale, Mask mask,
-                    int32_t win_left, int32_t win_right, void* stream) {
+                    int32_t win_left, int32_t win_right, void* stream,
+                    const uint8_t* kpm = nullptr) {
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (B < 1 || Nq < 1 || Nk < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B, Nq and Nk must be >= 1");
   fa_status st_ = check_common(H, d, softmax_scale);
@@ -186,7 +195,7 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
     st_ = check_strides(st[i], kTensorNames[i]);
     if (st_ != FA_OK) return st_;
   }
-  if (mask == Mask::kCausal && Nq != Nk)
+  if ((mask == Mask::kCausal || mask == Mask::kPadCausal) && Nq != Nk)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
   if (mask == Mask::kBand && (Nq > kMaxBandLen || Nk > kMaxBandLen))
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
@@ -217,6 +226,8 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   p.win_left = window_side(win_left, Nq, Nk);
   p.win_right = window_side(win_right, Nq, Nk);
   p.band_off = Nk - Nq;
+  p.kpm = kpm;
+  p.kpm_batch_stride = Nk;
   hipError_t e = launch<false>(p, d, dtype, mask, (uint32_t)grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
@@ -351,6 +362,19 @@ fa_status fa_fwd_varlen_band(const void* q, const void* k, const void* v, void* 
   contiguous(0, 0, H, d, st);
   return varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total, H, d, st,
                     FA_DTYPE_BF16, softmax_scale, Mask::kBand, window_left, window_right, stream);
+}
+
+fa_status fa_fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const uint8_t* key_padding_mask, int32_t B, int32_t S, int32_t H,
+                        int32_t d, int32_t dtype, float softmax_scale, int32_t causal,
+                        void* stream) {
+  g_last_error.clear();
+  if (!key_padding_mask) return fail(FA_ERR_INVALID_ARGUMENT, "null key_padding_mask");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  Strides st[4];
+  contiguous(S, S, H, d, st);
+  return dense_fwd(q, k, v, o, lse, B, S, S, H, d, st, dtype, softmax_scale,
+                   causal ? Mask::kPadCausal : Mask::kPad, -1, -1, stream, key_padding_mask);
 }
 
 fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,

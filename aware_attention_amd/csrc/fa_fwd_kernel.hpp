@@ -101,6 +101,10 @@ struct FwdParams {
   int32_t win_left;            // >= 0; an unbounded side is passed as max(Nq, Nk)
   int32_t win_right;           // >= 0; likewise (varlen: max_seqlen)
   int32_t band_off;            // Nk - Nq (dense), 0 (varlen)
+  // Key padding mask (KPM instances only, dense self-attention): token n of
+  // batch b is valid iff kpm[b * kpm_batch_stride + n] != 0.
+  const uint8_t* kpm;
+  int64_t kpm_batch_stride;
 };
 
 constexpr int kWaves = 8;                 // two groups of four
@@ -237,12 +241,15 @@ __device__ inline int band_tile_of_rank(int r, int n, int Nk, int band_lo, int b
   return left > right ? tc - m - rest : tc + 1 + m + rest;
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16>
+template <int D, bool CAUSAL, bool VARLEN, bool BAND, bool F16, bool KPM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D == 32 ? 4 : 2, D == 32 ? 4 : 2)))
 void fwd_kernel(FwdParams p) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
   static_assert(!(CAUSAL && BAND), "causal is the band (unbounded, 0)");
+  static_assert(!(KPM && (BAND || VARLEN)), "the key padding mask is for dense batches");
+  // A row can see no key at all (a band, or a padding mask).
+  constexpr bool EMPTY_ROWS = BAND || KPM;
   constexpr int BC = kBC;
   using TL = TileLayout<D>;
   constexpr int RB = TL::kRowBytes;
@@ -362,6 +369,14 @@ void fwd_kernel(FwdParams p) {
     const int w_hi = min(Nk - 1, min(Nq - 1, qw0 + 31) + band_hi);
     wave_first_kt = w_lo / BC;
     wave_last_kt = w_hi >= w_lo ? w_hi / BC : -1;
+  }
+  // Key padding mask: this batch's row of the mask, and whether this lane's
+  // query is a valid token (padding queries write O = 0, L = -inf).
+  const uint8_t* kpm_row = nullptr;
+  bool q_valid = true;
+  if constexpr (KPM) {
+    kpm_row = p.kpm + (int64_t)bidx * p.kpm_batch_stride;
+    q_valid = qrow < Nq && kpm_row[qrow] != 0;
   }
   bf16x8 qr[DS];
   if (qrow < Nq) {
@@ -527,7 +542,7 @@ void fwd_kernel(FwdParams p) {
   // Online softmax of one tile: s -> pb, updating m_run, l_run and (rarely) o.
   // Instantiated separately for tiles that need the mask and tiles that do
   // not, so the common path carries no per-element selects.
-  auto softmax_tile = [&](auto masked_tag, int k0) __attribute__((always_inline)) {
+  auto softmax_tile = [&](auto masked_tag, int k0, uint32_t kvalid) __attribute__((always_inline)) {
     constexpr bool masked = decltype(masked_tag)::value;
     float mt = kNegInf;
     if constexpr (masked) {
@@ -538,6 +553,7 @@ void fwd_kernel(FwdParams p) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
           bool ok = key < Nk && (!CAUSAL || key <= qrow);
           if constexpr (BAND) ok = ok && key >= qrow + band_lo && key <= qrow + band_hi;
+          if constexpr (KPM) ok = ok && ((kvalid >> (16 * kb + r)) & 1);
           s[kb][r] = ok ? s[kb][r] * s2 : kNegInf;
           mt = fmaxf(mt, s[kb][r]);
         }
@@ -558,7 +574,7 @@ void fwd_kernel(FwdParams p) {
       const float m_new = fmaxf(m_run, mt);
       // A band row that still sees no key has m_run = m_new = -inf; its
       // state is all zeros and stays so (alpha 1 instead of exp2(NaN)).
-      const float alpha = (BAND && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = (EMPTY_ROWS && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
@@ -566,7 +582,7 @@ void fwd_kernel(FwdParams p) {
     }
     // A row that has seen no key yet (band only) keeps m = -inf; its
     // exponentials are of -inf and must come out 0, not NaN.
-    const float neg_m = (BAND && m_run == kNegInf) ? 0.f : -m_run;
+    const float neg_m = (EMPTY_ROWS && m_run == kNegInf) ? 0.f : -m_run;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -593,13 +609,44 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
+  // Key padding mask of a tile: lane l reads the byte of key 64 kt + l, and a
+  // ballot gives the wave the tile's 64 validity bits. The byte of the wave's
+  // next tile is loaded one softmax ahead, so its latency hides behind a tile.
+  int kpm_kt = -1;
+  bool kpm_next = false;
+  auto kpm_byte = [&](int kt) __attribute__((always_inline)) -> bool {
+    const int key = kt * BC + lane;
+    return key < Nk && kpm_row[key] != 0;
+  };
+  // The 32 keys of a lane are the 4-key groups 8 g + 4 (l/32) + 0..3 of the
+  // tile (g = 0..7); their validity bits are gathered once per tile from the
+  // wave's 64 bits (scalar code), key 32 kb + 8 (r/4) + 4 (l/32) + r%4 of
+  // register r in block kb landing at bit 16 kb + r.
+  auto lane_bits = [&](uint64_t kbits) __attribute__((always_inline)) -> uint32_t {
+    auto gather = [](uint64_t x) -> uint32_t {   // nibble 2n of x -> nibble n
+      x &= 0x0F0F0F0F0F0F0F0Full;
+      x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
+      x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
+      return (uint32_t)(x | (x >> 16));
+    };
+    const uint32_t even = gather(kbits), odd = gather(kbits >> 4);
+    return hi ? odd : even;
+  };
   auto softmax = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
+    uint64_t kbits = ~0ull;
+    if constexpr (KPM) {
+      const bool cur = kpm_kt == kt ? kpm_next : kpm_byte(kt);
+      kpm_next = kpm_byte(kt + 1);
+      kpm_kt = kt + 1;
+      kbits = __builtin_amdgcn_ballot_w64(cur);
+    }
     if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0) ||
-        (BAND && (k0 < qw0 + 31 + band_lo || k0 + BC - 1 > qw0 + band_hi)))
-      softmax_tile(std::true_type{}, k0);
+        (BAND && (k0 < qw0 + 31 + band_lo || k0 + BC - 1 > qw0 + band_hi)) ||
+        (KPM && kbits != ~0ull))
+      softmax_tile(std::true_type{}, k0, KPM ? lane_bits(kbits) : 0u);
     else
-      softmax_tile(std::false_type{}, k0);
+      softmax_tile(std::false_type{}, k0, 0u);
   };
 
   auto active = [&](int kt) __attribute__((always_inline)) {
@@ -650,6 +697,7 @@ void fwd_kernel(FwdParams p) {
       js1 = max(js0, min(min(t_b, full_kt - 2), kt_end - 2) + 1);
     }
   }
+  if constexpr (KPM) js1 = js0;   // any tile may hold padding keys: no steady periods
   auto period = [&](int j) __attribute__((always_inline)) {
     if (!group_b) {
       if (j < kt_end) {
@@ -682,10 +730,10 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
         });
-        softmax_tile(std::false_type{}, 0);
+        softmax_tile(std::false_type{}, 0, 0u);
         __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
       } else {
-        softmax_tile(std::false_type{}, 0);
+        softmax_tile(std::false_type{}, 0, 0u);
         qk_pv(j, [] {});
       }
       barrier_nofence();
@@ -696,7 +744,8 @@ void fwd_kernel(FwdParams p) {
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Nq) {
-    const float inv = (BAND && l_tot == 0.f) ? 0.f : __builtin_amdgcn_rcpf(l_tot);
+    const bool empty = (EMPTY_ROWS && l_tot == 0.f) || !q_valid;
+    const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(l_tot);
     uint16_t* orow = p.o + o_off + (int64_t)qrow * o_ts;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -708,7 +757,7 @@ void fwd_kernel(FwdParams p) {
       }
     }
     if (hi == 0)
-      p.lse[l_off + qrow] = (BAND && l_tot == 0.f) ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      p.lse[l_off + qrow] = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 

@@ -81,9 +81,15 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0):
         per_head = spec.flops() / (spec.B * spec.H)
         for b, h in pairs:
             f64 = lambda x: W.bf16_bits_to_f32(x[b, :, h]).astype(np.float64)  # noqa: E731
-            attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal,
-                      window=spec.window)
-            flops += per_head
+            if "mask" in wl:   # padded batch: the valid tokens of row b (right padding)
+                n = int(wl["mask"][b].sum())
+                attention(f64(wl["q"])[:n], f64(wl["k"])[:n], f64(wl["v"])[:n], spec.scale,
+                          spec.causal)
+                flops += 4.0 * n * n * spec.d / (2 if spec.causal else 1)
+            else:
+                attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal,
+                          window=spec.window)
+                flops += per_head
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -185,14 +191,19 @@ def main():
                   "causal": spec.causal}
         if spec.window is not None:
             config["window"] = list(spec.window)
+        kpm = None
+        if "mask" in wl:
+            kpm = torch.from_numpy(wl["mask"]).cuda()
+            config["key_padding_mask"] = "right padding, lengths U{256..N}"
+            config["valid_tokens"] = int(wl["mask"].sum())
 
         def step():
             aa.fa_fwd(q, k, v, softmax_scale=spec.scale, causal=spec.causal, out=o, lse=lse,
-                      window=spec.window)
+                      window=spec.window, key_padding_mask=kpm)
 
         if args.backward:
-            if spec.window is not None:
-                print("the backward takes no window", file=sys.stderr)
+            if spec.window is not None or kpm is not None:
+                print("the backward takes no window or padding mask", file=sys.stderr)
                 sys.exit(2)
             step()
             do = to_dev(W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0])

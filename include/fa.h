@@ -186,6 +186,26 @@ fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, voi
                                 void* stream);
 
 /*
+ * Padded batch with a key padding mask (self-attention): the result of
+ * removing the padding positions, attending over the valid tokens of each
+ * batch row and putting the result back in the padded shape, computed in
+ * place without copies ("InternViT-6B-448px-V1-2 如何加速注意力计算", section
+ * FlashAttention 封装类三条执行路径, 带掩码路径).
+ *   q, k, v, o        : (B, S, H, d) dtype, densely packed; o written
+ *   lse               : (B, H, S) float32, written
+ *   key_padding_mask  : DEVICE uint8 (B, S); nonzero = valid token, 0 = padding
+ *   dtype, causal     : as in fa_fwd_strided; causal runs over the order of
+ *                       the valid tokens (query i sees valid keys j <= i)
+ * Padding positions get o = 0 and lse = -inf (they take no part in the
+ * attention). Tiles whose 64 keys are all valid take the unmasked path.
+ * Errors: as fa_fwd_strided; a null mask is FA_ERR_INVALID_ARGUMENT.
+ */
+fa_status fa_fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const uint8_t* key_padding_mask, int32_t B, int32_t S, int32_t H,
+                        int32_t d, int32_t dtype, float softmax_scale, int32_t causal,
+                        void* stream);
+
+/*
  * Backward pass, equal-length batch: the gradients of O with respect to Q, K
  * and V for an incoming gradient dO, with S and P recomputed from the saved
  * log-sum-exp instead of stored ("FlashAttention/zh" (marovi.ai wiki),

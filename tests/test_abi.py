@@ -332,3 +332,30 @@ def test_bwd_valid_calls_without_a_device_are_hip_errors():
     assert _bwd(causal=1, dtype=_lib.FA_DTYPE_F16) == HIP
     assert _bwd_varlen() == HIP
     assert _bwd_varlen(total=0, max_seqlen=0) == _lib.FA_OK
+
+
+def _padded(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, mask=P, B=2, S=100, H=2, d=64, dtype=_lib.FA_DTYPE_BF16,
+             scale=0.125, causal=0, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_fwd_padded(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["B"],
+                                  a["S"], a["H"], a["d"], a["dtype"], a["scale"], a["causal"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), INV), (dict(q=None), INV), (dict(causal=2), INV), (dict(dtype=5), INV),
+    (dict(S=0), INV), (dict(B=0), INV), (dict(o=P + 2), INV), (dict(d=80), UNS),
+])
+def test_fa_fwd_padded_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _padded(**kw) == code
+
+
+def test_padded_valid_call_without_a_device_is_a_hip_error():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _padded() == HIP
+    assert _padded(causal=1, dtype=_lib.FA_DTYPE_F16, mask=P + 1) == HIP   # mask bytes unaligned

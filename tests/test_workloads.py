@@ -111,3 +111,13 @@ def test_dense_f16_takes_the_same_draws():
     # both round the same float32 draws: they agree to bf16 precision
     assert np.allclose(W.bf16_bits_to_f32(qb), W.f16_bits_to_f32(qh), rtol=2**-7, atol=1e-6)
     assert not np.array_equal(qb, qh)
+
+
+def test_padded_workload_recipe():
+    wl = W.make_workload("vitpad")
+    spec = wl["spec"]
+    n = spec.pad_lengths()
+    assert wl["mask"].shape == (32, 1025) and n.min() >= 256 and n.max() <= 1025
+    assert np.array_equal(wl["mask"].sum(axis=1), n)
+    assert np.all(wl["mask"][np.arange(32), n - 1] == 1)
+    assert spec.flops() == pytest.approx(4.0 * float(np.sum(n.astype(float) ** 2)) * 128 * 25)

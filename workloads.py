@@ -14,6 +14,8 @@ Workloads (shapes follow the pages' models):
   prefill2k   B=4  H=32 N=2048 d=128  causal                 seed 55
   band8k      B=1  H=32 N=8192 d=128  band (2047, 0): each query sees itself
               and the 2047 keys before it                    seed 6
+  vitpad      the vit batch with a key padding mask: row b keeps its first
+              n_b ~ U{256..1025} tokens (lengths seed 10), the rest is padding
 
 The detector token counts (40x40, 20x20 and the 4-head, 32-wide head split)
 come from "YOLOv12官版镜像集成Flash Attention v2，提速原理浅析" (sections 2.1 and
@@ -85,14 +87,25 @@ class Dense:
     seed: int
     rms_qk: bool = False
     window: tuple | None = None   # banded mask (left, right), None = unbounded side
+    pad_seed: int | None = None   # key padding mask: right padding to lengths
+                                  # drawn U{256..N} with this seed
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
+    def pad_lengths(self) -> np.ndarray:
+        """Valid tokens per batch row of a padded workload."""
+        return varlen_lengths(self.B, 256, self.N, self.pad_seed)
+
     def flops(self) -> float:
         """Useful FLOPs: 4 d per (query, visible key) pair, the causal count
-        taken as N^2 / 2, the band's as its exact pair count."""
+        taken as N^2 / 2, the band's as its exact pair count, a padded batch's
+        over its valid tokens only."""
+        if self.pad_seed is not None:
+            n = self.pad_lengths().astype(np.float64)
+            f = 4.0 * float(np.sum(n * n)) * self.d * self.H
+            return f / 2 if self.causal else f
         if self.window is not None:
             return 4.0 * band_pairs(self.N, self.N, self.window) * self.d * self.H * self.B
         f = 4.0 * self.N * self.N * self.d * self.H * self.B
@@ -131,6 +144,8 @@ WORKLOADS = {
     "prefill2k": Dense("prefill2k", B=4, H=32, N=2048, d=128, causal=True, seed=55),
     "band8k": Dense("band8k", B=1, H=32, N=8192, d=128, causal=False, seed=6,
                     window=(2047, 0)),
+    "vitpad": Dense("vitpad", B=32, H=25, N=1025, d=128, causal=False, seed=3, rms_qk=True,
+                    pad_seed=10),
 }
 
 
@@ -220,8 +235,12 @@ def make_workload(name: str):
     w = WORKLOADS[name]
     if isinstance(w, Dense):
         q, k, v = make_dense(w.B, w.N, w.H, w.d, w.seed, rms_qk=w.rms_qk)
-        return dict(q=q, k=k, v=v, scale=w.scale, causal=w.causal,
-                    shape=(w.B, w.N, w.H, w.d), spec=w)
+        out = dict(q=q, k=k, v=v, scale=w.scale, causal=w.causal,
+                   shape=(w.B, w.N, w.H, w.d), spec=w)
+        if w.pad_seed is not None:
+            n = w.pad_lengths()
+            out["mask"] = (np.arange(w.N)[None, :] < n[:, None]).astype(np.uint8)
+        return out
     rng = np.random.default_rng(w.seed)
     lengths = rng.integers(w.len_lo, w.len_hi + 1, size=w.num_seqs).astype(np.int64)
     q, k, v, cu = make_varlen(lengths, w.H, w.d, w.seed, rng=rng)
