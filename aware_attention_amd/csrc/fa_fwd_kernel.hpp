@@ -356,11 +356,63 @@ void fwd_kernel(FwdParams p) {
     kt0 = k_lo / BC;
     kt_end = k_hi >= k_lo ? k_hi / BC + 1 : kt0;
   }
+  // Key padding mask: the valid tokens of this batch row lie in [kv_lo,
+  // kv_hi] (one pass over the row's mask by the whole workgroup). Key tiles
+  // outside that span hold only padding and are skipped; a query tile outside
+  // it holds only padding rows and does no work at all.
+  // kv_run: the valid tokens form one run (no padding inside the span).
+  const uint8_t* kpm_row = nullptr;
+  int kv_lo = 0, kv_hi = Nk - 1;
+  bool kv_run = true;
+  if constexpr (KPM) {
+    kpm_row = p.kpm + (int64_t)bidx * p.kpm_batch_stride;
+    int lo = Nk, hi_ = -1, cnt = 0;
+    for (int i = tid; i < Nk; i += kThreads) {
+      if (kpm_row[i] != 0) {
+        lo = min(lo, i);
+        hi_ = max(hi_, i);
+        ++cnt;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off, 64));
+      hi_ = max(hi_, __shfl_xor(hi_, off, 64));
+      cnt += __shfl_xor(cnt, off, 64);
+    }
+    int* red = reinterpret_cast<int*>(smem);   // no tile has been copied yet
+    if (lane == 0) {
+      red[3 * wave] = lo;
+      red[3 * wave + 1] = hi_;
+      red[3 * wave + 2] = cnt;
+    }
+    __syncthreads();
+    lo = Nk;
+    hi_ = -1;
+    cnt = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      lo = min(lo, red[3 * w]);
+      hi_ = max(hi_, red[3 * w + 1]);
+      cnt += red[3 * w + 2];
+    }
+    __syncthreads();   // before the tile copies reuse the LDS
+    kv_lo = lo;
+    kv_hi = hi_;
+    kv_run = cnt == hi_ - lo + 1;
+    if (hi_ < lo || q0 > hi_ || q0 + kBR - 1 < lo) {
+      kt_end = kt0;    // no valid key, or no valid query in this tile
+    } else {
+      kt0 = max(kt0, lo / BC);
+      kt_end = min(kt_end, hi_ / BC + 1);
+    }
+  }
 
   // ---- Q rows of this lane, kept in VGPRs ----
   const int qw0 = q0 + wave * 32;        // first query row of this wavefront
   const int qrow = qw0 + l32;            // this lane's query row
-  const bool wave_has_rows = qw0 < Nq;
+  // (With a padding mask, a wave whose rows all lie outside the valid span
+  // has only padding rows: it skips the work and writes zeros.)
+  const bool wave_has_rows = qw0 < Nq && (!KPM || (qw0 <= kv_hi && qw0 + 31 >= kv_lo));
   // First and last key tiles with a visible key for some row of this wavefront.
   int wave_first_kt = 0;
   int wave_last_kt = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BC) : n_kt - 1;
@@ -372,12 +424,8 @@ void fwd_kernel(FwdParams p) {
   }
   // Key padding mask: this batch's row of the mask, and whether this lane's
   // query is a valid token (padding queries write O = 0, L = -inf).
-  const uint8_t* kpm_row = nullptr;
   bool q_valid = true;
-  if constexpr (KPM) {
-    kpm_row = p.kpm + (int64_t)bidx * p.kpm_batch_stride;
-    q_valid = qrow < Nq && kpm_row[qrow] != 0;
-  }
+  if constexpr (KPM) q_valid = qrow < Nq && kpm_row[qrow] != 0;
   bf16x8 qr[DS];
   if (qrow < Nq) {
     const u32x4* src = reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * q_ts);
@@ -697,7 +745,19 @@ void fwd_kernel(FwdParams p) {
       js1 = max(js0, min(min(t_b, full_kt - 2), kt_end - 2) + 1);
     }
   }
-  if constexpr (KPM) js1 = js0;   // any tile may hold padding keys: no steady periods
+  if constexpr (KPM) {
+    // Steady periods only when the valid tokens form one run and this query
+    // tile lies inside it (every wave active): then tiles whose keys all lie
+    // in the run need no mask. Otherwise every period takes the general path.
+    js0 = kt0 + 1;
+    js1 = js0;
+    if (kv_run && q0 >= kv_lo && q0 + kBR - 1 <= kv_hi) {
+      const int t_a = (kv_lo + BC - 1) / BC;   // first tile with all keys valid
+      const int t_b = (kv_hi + 1) / BC - 1;    // last one
+      js0 = max(js0, t_a + 1);
+      js1 = max(js0, min(min(t_b, unmasked_kt - 1), min(full_kt - 2, kt_end - 2)) + 1);
+    }
+  }
   auto period = [&](int j) __attribute__((always_inline)) {
     if (!group_b) {
       if (j < kt_end) {

@@ -244,7 +244,9 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    assert torch.isfinite(lse).all(), "non-finite log-sum-exp in the timed output"
+    # rows that see no key (padding positions, empty band rows) have L = -inf
+    assert not torch.isnan(lse).any() and not torch.isposinf(lse).any(), \
+        "NaN or +inf log-sum-exp in the timed output"
 
     traffic = read_traffic(args.workload + ("_bwd" if args.backward else ""))
     out = {
