@@ -10,6 +10,7 @@
 #include <mutex>
 #include <string>
 
+#include "fa_fwd256_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
 #include "fa_host.hpp"
 
@@ -99,12 +100,30 @@ hipError_t launch_t(const fa::FwdParams& p, int d, Mask mask, uint32_t grid, hip
   }
 }
 
+// Head dimension 256 (unmasked or causal): its own kernel, 128-row tiles.
+template <bool VARLEN, bool F16>
+hipError_t launch_256(const fa::FwdParams& p, Mask mask, uint32_t grid, hipStream_t stream) {
+  if (mask == Mask::kCausal)
+    hipLaunchKernelGGL((fa::fwd256_kernel<true, VARLEN, F16>), dim3(grid), dim3(fa::kBwdThreads),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((fa::fwd256_kernel<false, VARLEN, F16>), dim3(grid), dim3(fa::kBwdThreads),
+                       0, stream, p);
+  return hipGetLastError();
+}
+
 template <bool VARLEN>
 hipError_t launch(const fa::FwdParams& p, int d, int32_t dtype, Mask mask, uint32_t grid,
                   hipStream_t stream) {
+  if (d == 256)
+    return dtype == FA_DTYPE_F16 ? launch_256<VARLEN, true>(p, mask, grid, stream)
+                                 : launch_256<VARLEN, false>(p, mask, grid, stream);
   return dtype == FA_DTYPE_F16 ? launch_t<VARLEN, true>(p, d, mask, grid, stream)
                                : launch_t<VARLEN, false>(p, d, mask, grid, stream);
 }
+
+// Query rows per workgroup of the kernel that serves head dimension d.
+int rows_per_workgroup(int d) { return d == 256 ? fa::kRows256 : fa::kBR; }
 
 // Window sides: >= 0, or -1 for unbounded. A side of max(nq, nk) already
 // reaches every key (left needs Nk - 1 at most, right Nq - 1), so -1 and any
@@ -165,7 +184,15 @@ fa_status check_common(int32_t H, int32_t d, float scale) {
   if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
-  if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
+  if (d != 32 && d != 64 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64, 128 or 256");
+  return FA_OK;
+}
+
+// Head dimension 256 runs unmasked or causal only.
+fa_status check_d256(int32_t d, Mask mask) {
+  if (d == 256 && mask != Mask::kNone && mask != Mask::kCausal)
+    return fail(FA_ERR_UNSUPPORTED, "head dim 256 supports no band or padding mask");
   return FA_OK;
 }
 
@@ -197,11 +224,13 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   }
   if ((mask == Mask::kCausal || mask == Mask::kPadCausal) && Nq != Nk)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
+  st_ = check_d256(d, mask);
+  if (st_ != FA_OK) return st_;
   if (mask == Mask::kBand && (Nq > kMaxBandLen || Nk > kMaxBandLen))
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
-  const int64_t n_qt = (Nq + fa::kBR - 1) / fa::kBR;
+  const int64_t n_qt = (Nq + rows_per_workgroup(d) - 1) / rows_per_workgroup(d);
   const int64_t grid = n_qt * H * (int64_t)B;
   if (grid > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many query tiles for one launch");
   st_ = check_device();
@@ -254,12 +283,14 @@ fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float
   }
   if (mask == Mask::kBand && max_seqlen > kMaxBandLen)
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports max_seqlen <= 2^29");
+  st_ = check_d256(d, mask);
+  if (st_ != FA_OK) return st_;
   if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned (cu_seqlens 4-byte)");
-  const int64_t n_qt = (max_seqlen + fa::kBR - 1) / fa::kBR;
+  const int64_t n_qt = (max_seqlen + rows_per_workgroup(d) - 1) / rows_per_workgroup(d);
   const int64_t grid = n_qt * H * (int64_t)num_seqs;
   if (grid > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many query tiles for one launch");
   st_ = check_device();

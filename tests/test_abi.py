@@ -75,7 +75,7 @@ def _varlen(**kw):
     (dict(causal=2), INV), (dict(causal=1, Nq=128, Nk=64), INV),
     (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
     (dict(q=P + 8), INV), (dict(o=P + 2), INV), (dict(lse=P + 4), INV),
-    (dict(d=48), UNS), (dict(d=256), UNS), (dict(scale=-0.5), UNS),
+    (dict(d=48), UNS), (dict(d=192), UNS), (dict(d=512), UNS), (dict(scale=-0.5), UNS),
 ])
 def test_fa_fwd_rejects_bad_arguments(kw, code):
     _lib_or_skip()
@@ -247,7 +247,7 @@ def test_fa_fwd_strided_rejects_bad_arguments(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(qs=None), INV), (dict(ks=(3 * 2 * 128, 129)), INV), (dict(dtype=7), INV),
-    (dict(causal=1, right=0), INV), (dict(cu=None), INV), (dict(d=256), UNS),
+    (dict(causal=1, right=0), INV), (dict(cu=None), INV), (dict(d=96), UNS),
 ])
 def test_fa_fwd_varlen_strided_rejects_bad_arguments(kw, code):
     _lib_or_skip()
@@ -359,3 +359,21 @@ def test_padded_valid_call_without_a_device_is_a_hip_error():
         pytest.skip("a GPU is present; this case covers hosts without one")
     assert _padded() == HIP
     assert _padded(causal=1, dtype=_lib.FA_DTYPE_F16, mask=P + 1) == HIP   # mask bytes unaligned
+
+
+def test_head_dim_256_checks():
+    """d = 256 runs unmasked, causal and varlen; bands, padding masks and the
+    backward reject it on the host."""
+    _lib_or_skip()
+    assert _band(d=256) == UNS
+    assert _padded(d=256) == UNS
+    assert _varlen_band(d=256) == UNS
+    assert _bwd(d=256) == UNS
+    assert _strided(d=256, left=0, right=3) == UNS
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        return
+    assert _fwd(d=256) == HIP and _fwd(d=256, causal=1) == HIP
+    assert _varlen(d=256) == HIP
+    assert _strided(d=256, qs=(100 * 3 * 256, 3 * 256, 256), ks=(80 * 3 * 256, 3 * 256, 256),
+                    vs=(80 * 3 * 256, 3 * 256, 256), os=(100 * 3 * 256, 3 * 256, 256)) == HIP

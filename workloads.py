@@ -14,6 +14,7 @@ Workloads (shapes follow the pages' models):
   prefill2k   B=4  H=32 N=2048 d=128  causal                 seed 55
   band8k      B=1  H=32 N=8192 d=128  band (2047, 0): each query sees itself
               and the 2047 keys before it                    seed 6
+  prefill8k_d256  B=1 H=16 N=8192 d=256 causal (prefill8k's FLOPs at head dim 256)  seed 7
   vitpad      the vit batch with a key padding mask: row b keeps its first
               n_b ~ U{256..1025} tokens (lengths seed 10), the rest is padding
 
@@ -144,6 +145,7 @@ WORKLOADS = {
     "prefill2k": Dense("prefill2k", B=4, H=32, N=2048, d=128, causal=True, seed=55),
     "band8k": Dense("band8k", B=1, H=32, N=8192, d=128, causal=False, seed=6,
                     window=(2047, 0)),
+    "prefill8k_d256": Dense("prefill8k_d256", B=1, H=16, N=8192, d=256, causal=True, seed=7),
     "vitpad": Dense("vitpad", B=32, H=25, N=1025, d=128, causal=False, seed=3, rms_qk=True,
                     pad_seed=10),
 }
