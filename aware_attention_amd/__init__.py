@@ -26,6 +26,9 @@ library is missing or the device is not a gfx950, calls raise.
         recomputed from lse; delta = rowsum(dout * o), laid out like lse.
     o = attention(q, k, v, softmax_scale=None, causal=False)
         forward with autograd: o.backward(...) runs fa_bwd.
+    o, lse = fa_decode(q, k, v, seqlens_k=None, softmax_scale=None)
+        one query per (batch, head), q (B,1,H,d), k/v (B,Nk,H,d) the cache, split
+        over the cache and merged through the log-sum-exps (fa_decode).
 
 The default scale is 1/sqrt(d), as in the definition on "FlashAttention/zh"
 (marovi.ai wiki), section 為何標準注意力運行緩慢. Only half precision on the
@@ -38,12 +41,14 @@ from __future__ import annotations
 import math
 
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
-                   FA_ERR_UNSUPPORTED, FA_OK, FaError, check, load, raw_fa_bwd, raw_fa_bwd_varlen,
+                   FA_ERR_UNSUPPORTED, FA_OK, FaError, check, decode_workspace_bytes, load,
+                   raw_fa_bwd, raw_fa_bwd_varlen, raw_fa_decode,
                    raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
                    raw_fa_fwd_varlen,
                    raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
 
-__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "attention", "FaError", "load",
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_decode", "attention",
+           "FaError", "load",
            "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
 
 
@@ -315,3 +320,45 @@ def attention(q, k, v, softmax_scale=None, causal=False):
     if _ATTENTION_FN is None:
         _ATTENTION_FN = _autograd_function()
     return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal)
+
+
+def fa_decode(q, k, v, seqlens_k=None, softmax_scale=None, out=None, lse=None, workspace=None):
+    """Decode step: q (B, 1, H, d), k/v (B, Nk, H, d); returns (o (B, 1, H, d), lse (B, H)).
+    seqlens_k: optional int32 (B,) on the device, the valid cache length per batch.
+    workspace: optional uint8 device tensor of at least decode_workspace_bytes(...) bytes
+    (allocated here through torch when None)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, 4)
+    B, one, H, d = q.shape
+    Nk = k.shape[1]
+    if one != 1 or k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != d:
+        raise ValueError(f"decode needs q (B,1,H,d) and k, v (B,Nk,H,d): q {tuple(q.shape)} "
+                         f"k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if not all(t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k and v must be contiguous for the decode")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H)")
+    sl = 0
+    if seqlens_k is not None:
+        if not isinstance(seqlens_k, torch.Tensor) or seqlens_k.dtype != torch.int32 \
+                or tuple(seqlens_k.shape) != (B,) or seqlens_k.device != q.device:
+            raise ValueError("seqlens_k must be an int32 tensor of shape (B,) on q's device")
+        sl = seqlens_k.data_ptr()
+    need = decode_workspace_bytes(B, Nk, H, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        check(raw_fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), sl or None, B, Nk, H, d, _dtype_code(q.dtype),
+                            _scale(softmax_scale, d), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), stream))
+    return out, lse

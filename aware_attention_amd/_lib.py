@@ -18,7 +18,8 @@ FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
-            "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_status_string",
+            "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_decode",
+            "fa_decode_workspace_bytes", "fa_status_string",
             "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -60,6 +61,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen_strided.restype = i32
     lib.fa_fwd_padded.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_padded.restype = i32
+    lib.fa_decode.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
+    lib.fa_decode.restype = i32
+    lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_bwd_varlen.argtypes = [vp] * 11 + [i32, i32, i32, i32, i32, i32, f32, i32, vp]
@@ -149,3 +154,14 @@ def raw_fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs, ma
 def raw_fa_fwd_padded(q, k, v, o, lse, mask, B, S, H, d, dtype, scale, causal, stream) -> int:
     """Pointer-level call of fa_fwd_padded; returns the status code."""
     return load().fa_fwd_padded(q, k, v, o, lse, mask, B, S, H, d, dtype, scale, causal, stream)
+
+
+def raw_fa_decode(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, scale, workspace,
+                  workspace_bytes, stream) -> int:
+    """Pointer-level call of fa_decode; returns the status code."""
+    return load().fa_decode(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, scale, workspace,
+                            workspace_bytes, stream)
+
+
+def decode_workspace_bytes(B, Nk, H, d) -> int:
+    return int(load().fa_decode_workspace_bytes(B, Nk, H, d))

@@ -22,8 +22,8 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17",
 
 
 # Translation units of libfa.so: the forward entry points and host helpers,
-# and the backward entry points. They compile in parallel, then link.
-SOURCES = ["fa_api.hip", "fa_bwd_api.hip"]
+# the backward entry points and the decode. They compile in parallel, then link.
+SOURCES = ["fa_api.hip", "fa_bwd_api.hip", "fa_decode_api.hip"]
 _NOISE = "is not a recognized feature for this target"
 
 

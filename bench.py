@@ -33,6 +33,8 @@ import workloads as W  # noqa: E402
 
 METRIC = "attention fwd TFLOPS (bf16) and % of MFMA peak, N=1025..8192, d=128"
 METRIC_BWD = "attention bwd TFLOPS (bf16) and % of MFMA peak"
+METRIC_DECODE = "attention decode HBM GB/s (bf16, one query per head)"
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 KERNEL_SOURCES = [os.path.join(ROOT, "aware_attention_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_api.hip")]
@@ -141,6 +143,28 @@ def cpu_baseline_bwd(wl: dict, budget_s: float = 12.0):
                                         f"backward, float64 numpy, {dt:.1f} s"}
 
 
+def cpu_baseline_decode(wl: dict, budget_s: float = 12.0):
+    """Time the float64 oracle on whole (batch, head) decode rows until budget_s is used;
+    reported in GB/s of the same compulsory bytes."""
+    from oracle import attention
+    spec = wl["spec"]
+    per_head = spec.bytes_compulsory() / (spec.B * spec.H)
+    done, t0 = 0, time.perf_counter()
+    for b in range(spec.B):
+        for h in range(spec.H):
+            f64 = lambda x: W.bf16_bits_to_f32(x[b, :, h]).astype(np.float64)  # noqa: E731
+            attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * per_head / dt / 1e9, "unit": "GB/s", "cores": os.cpu_count() or 1,
+            "kind": "oracle", "sample": f"{done} of {spec.B * spec.H} (batch, head) rows, "
+                                        f"float64 numpy, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +208,21 @@ def main():
     to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
     q, k, v = to_dev(wl["q"]), to_dev(wl["k"]), to_dev(wl["v"])
     o = torch.empty_like(q)
-    if isinstance(spec, W.Dense):
+    decode = isinstance(spec, W.Decode)
+    if decode:
+        if args.backward:
+            print("--backward is measured on equal-length workloads", file=sys.stderr)
+            sys.exit(2)
+        lse = torch.empty((spec.B, spec.H), dtype=torch.float32, device="cuda")
+        flops = spec.flops()
+        config = {"workload": args.workload, "B": spec.B, "H": spec.H, "Nk": spec.Nk, "d": spec.d,
+                  "queries_per_head": 1}
+        ws = torch.empty(aa._lib.decode_workspace_bytes(spec.B, spec.Nk, spec.H, spec.d),
+                         dtype=torch.uint8, device="cuda")
+
+        def step():
+            aa.fa_decode(q, k, v, softmax_scale=spec.scale, out=o, lse=lse, workspace=ws)
+    elif isinstance(spec, W.Dense):
         lse = torch.empty((spec.B, spec.H, spec.N), dtype=torch.float32, device="cuda")
         flops = spec.flops()
         config = {"workload": args.workload, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
@@ -249,6 +287,21 @@ def main():
         "NaN or +inf log-sum-exp in the timed output"
 
     traffic = read_traffic(args.workload + ("_bwd" if args.backward else ""))
+    if decode:
+        gbs = spec.bytes_compulsory() / (ms_per_step * 1e-3) / 1e9
+        out = {
+            "metric": METRIC_DECODE, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16, shapes of the workload)", "config": config,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
+            "tflops": round(tflops, 2), "wall_s_timed": round(wall, 4),
+        }
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_decode(wl)
+        print(json.dumps(out), flush=True)
+        return
     out = {
         "metric": METRIC_BWD if args.backward else METRIC,
         "value": round(tflops, 2),

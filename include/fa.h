@@ -45,6 +45,7 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -242,6 +243,35 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
                         int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
                         float softmax_scale, int32_t causal, void* stream);
+
+/*
+ * Decode: one query per (batch, head) against a KV cache, the step of token
+ * generation. The scores are a matrix-vector product, so the cache is split
+ * into chunks processed by separate workgroups, and the partial results
+ * (O_s, L_s) are merged exactly through their log-sum-exps:
+ * L = ln sum_s e^{L_s}, O = sum_s e^{L_s - L} O_s (the forward's L = m + log l,
+ * "FlashAttention/zh" (marovi.ai wiki), section FlashAttention 算法).
+ *   q, o      : (B, 1, H, d) dtype, densely packed; o written
+ *   k, v      : (B, Nk, H, d) dtype, the cache, densely packed
+ *   lse       : (B, H) float32, written (natural log)
+ *   seqlens_k : DEVICE int32[B] or NULL; batch b attends to its first
+ *               min(max(seqlens_k[b], 0), Nk) keys (NULL: all Nk). A batch
+ *               with no key gets o = 0 and lse = -inf.
+ *   workspace : DEVICE buffer of at least fa_decode_workspace_bytes(B, Nk, H,
+ *               d) bytes, 16-byte aligned, owned by the caller (the partial
+ *               results; the library allocates nothing). Calls that overlap on
+ *               one workspace race.
+ * Scores, softmax and P V are computed in fp32 (no 16-bit rounding of P).
+ * Errors: as fa_fwd_strided; a null or too small workspace is
+ * FA_ERR_INVALID_ARGUMENT; d must be 32, 64, 128 or 256.
+ */
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* seqlens_k, int32_t B, int32_t Nk, int32_t H, int32_t d,
+                    int32_t dtype, float softmax_scale, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes fa_decode needs for these sizes (0 for sizes below 1). */
+size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d);
 
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int32_t status);

@@ -377,3 +377,44 @@ def test_head_dim_256_checks():
     assert _varlen(d=256) == HIP
     assert _strided(d=256, qs=(100 * 3 * 256, 3 * 256, 256), ks=(80 * 3 * 256, 3 * 256, 256),
                     vs=(80 * 3 * 256, 3 * 256, 256), os=(100 * 3 * 256, 3 * 256, 256)) == HIP
+
+
+def _decode(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, sl=None, B=2, Nk=1000, H=4, d=128,
+             dtype=_lib.FA_DTYPE_BF16, scale=0.088, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["sl"], a["B"], a["Nk"],
+                              a["H"], a["d"], a["dtype"], a["scale"], a["ws"], a["wsb"],
+                              a["stream"])
+
+
+def test_decode_workspace_plan():
+    _lib_or_skip()
+    ws = _lib.decode_workspace_bytes
+    assert ws(0, 10, 1, 64) == 0 and ws(1, 0, 1, 64) == 0
+    assert ws(1, 100, 1, 64) == 1 * 1 * 1 * 65 * 4              # one chunk of 128 keys
+    # 1 x 1 head, 8192 keys: chunks of >= 256 keys -> 32 splits
+    assert ws(1, 8192, 1, 128) == 32 * 129 * 4
+    # 16 x 32 heads = 512 units: 4 splits each reach 2048 workgroups
+    assert ws(16, 8192, 32, 128) == 16 * 32 * 4 * 129 * 4
+    # a long cache is cut into chunks of at most 4096 keys
+    assert ws(64, 100000, 32, 128) == 64 * 32 * 25 * 129 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(ws=None), INV), (dict(wsb=100), INV), (dict(B=0), INV),
+    (dict(Nk=0), INV), (dict(H=0), INV), (dict(dtype=9), INV), (dict(scale=float("inf")), INV),
+    (dict(d=48), UNS), (dict(sl=P + 2), INV), (dict(ws=P + 8), INV),
+])
+def test_fa_decode_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _decode(**kw) == code
+
+
+def test_decode_valid_call_without_a_device_is_a_hip_error():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _decode() == HIP
+    assert _decode(d=256, sl=P, dtype=_lib.FA_DTYPE_F16) == HIP

@@ -247,3 +247,20 @@ def test_padded_keys_ignore_padding_content():
         O2, L2 = attention_padded(q2, k2, v2, mask, 0.7, causal)
         np.testing.assert_array_equal(O1, O2)
         np.testing.assert_array_equal(L1, L2)
+
+
+def test_lse_merge_of_key_chunks_is_attention():
+    """Attention over all keys equals the merge of attention over disjoint key
+    chunks through their log-sum-exps: L = ln sum_s e^{L_s}, O = sum_s e^{L_s - L} O_s
+    (the use of L beyond the backward; the split decode relies on it)."""
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((1, 8))
+    k, v = rng.standard_normal((37, 8)), rng.standard_normal((37, 5))
+    O, L = attention(q, k, v, 0.4)
+    for bounds in ([0, 37], [0, 10, 37], [0, 1, 2, 30, 37], [0, 5, 5, 37]):
+        parts = [attention(q, k[a:b], v[a:b], 0.4) for a, b in zip(bounds, bounds[1:]) if b > a]
+        Ls = np.array([p[1][0] for p in parts])
+        Lm = np.log(np.sum(np.exp(Ls - Ls.max()))) + Ls.max()
+        Om = sum(np.exp(p[1][0] - Lm) * p[0][0] for p in parts)
+        np.testing.assert_allclose(Om, O[0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(Lm, L[0], rtol=0, atol=1e-13)

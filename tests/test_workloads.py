@@ -121,3 +121,13 @@ def test_padded_workload_recipe():
     assert np.array_equal(wl["mask"].sum(axis=1), n)
     assert np.all(wl["mask"][np.arange(32), n - 1] == 1)
     assert spec.flops() == pytest.approx(4.0 * float(np.sum(n.astype(float) ** 2)) * 128 * 25)
+
+
+def test_decode_workload_recipe():
+    wl = W.make_workload("decode8k")
+    spec = wl["spec"]
+    assert wl["q"].shape == (16, 1, 32, 128) and wl["k"].shape == (16, 8192, 32, 128)
+    assert spec.bytes_compulsory() == 2 * 16 * 8192 * 32 * 128 * 2 + 2 * 16 * 32 * 128 * 2 + 16 * 32 * 4
+    rng = np.random.default_rng(spec.seed)
+    q = W.f32_to_bf16_bits(rng.standard_normal((16, 1, 32, 128), dtype=np.float32))
+    assert np.array_equal(q, wl["q"])

@@ -14,6 +14,9 @@ Workloads (shapes follow the pages' models):
   prefill2k   B=4  H=32 N=2048 d=128  causal                 seed 55
   band8k      B=1  H=32 N=8192 d=128  band (2047, 0): each query sees itself
               and the 2047 keys before it                    seed 6
+  decode8k    B=16 H=32 d=128: one query per (batch, head), 8192-key cache   seed 8
+  decode32k   B=4  H=32 d=128: one query per (batch, head), 32768-key cache  seed 9
+              (q drawn first with the seed, then K and V of the cache)
   prefill8k_d256  B=1 H=16 N=8192 d=256 causal (prefill8k's FLOPs at head dim 256)  seed 7
   vitpad      the vit batch with a key padding mask: row b keeps its first
               n_b ~ U{256..1025} tokens (lengths seed 10), the rest is padding
@@ -134,6 +137,30 @@ class Varlen:
         return 1.0 / math.sqrt(self.d)
 
 
+@dataclasses.dataclass(frozen=True)
+class Decode:
+    """One query per (batch, head) against a KV cache: q, o (B, 1, H, d),
+    k, v (B, Nk, H, d), every cache entry valid."""
+    name: str
+    B: int
+    H: int
+    Nk: int
+    d: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def bytes_compulsory(self) -> int:
+        """HBM bytes a decode step must move: K and V once, q and o, L."""
+        return 2 * self.B * self.Nk * self.H * self.d * 2 + 2 * self.B * self.H * self.d * 2 \
+            + self.B * self.H * 4
+
+    def flops(self) -> float:
+        return 4.0 * self.B * self.H * self.Nk * self.d
+
+
 WORKLOADS = {
     "tiny": Dense("tiny", B=1, H=2, N=128, d=64, causal=False, seed=1),
     "det1600": Dense("det1600", B=16, H=4, N=1600, d=32, causal=False, seed=2),
@@ -146,6 +173,8 @@ WORKLOADS = {
     "band8k": Dense("band8k", B=1, H=32, N=8192, d=128, causal=False, seed=6,
                     window=(2047, 0)),
     "prefill8k_d256": Dense("prefill8k_d256", B=1, H=16, N=8192, d=256, causal=True, seed=7),
+    "decode8k": Decode("decode8k", B=16, H=32, Nk=8192, d=128, seed=8),
+    "decode32k": Decode("decode32k", B=4, H=32, Nk=32768, d=128, seed=9),
     "vitpad": Dense("vitpad", B=32, H=25, N=1025, d=128, causal=False, seed=3, rms_qk=True,
                     pad_seed=10),
 }
@@ -235,6 +264,12 @@ def make_workload(name: str):
     Varlen -> dict(q, k, v, cu_seqlens, max_seqlen, scale, causal, lengths).
     """
     w = WORKLOADS[name]
+    if isinstance(w, Decode):
+        rng = np.random.default_rng(w.seed)
+        q = _round(_draw(rng, (w.B, 1, w.H, w.d)), "bf16")
+        k = _round(_draw(rng, (w.B, w.Nk, w.H, w.d)), "bf16")
+        v = _round(_draw(rng, (w.B, w.Nk, w.H, w.d)), "bf16")
+        return dict(q=q, k=k, v=v, scale=w.scale, spec=w)
     if isinstance(w, Dense):
         q, k, v = make_dense(w.B, w.N, w.H, w.d, w.seed, rms_qk=w.rms_qk)
         out = dict(q=q, k=k, v=v, scale=w.scale, causal=w.causal,
