@@ -19,10 +19,11 @@ Contents:
 from .attention import (attention, attention_probs, attention_dense,
                         attention_varlen, ORACLE_DTYPE)
 from .backward import (attention_backward, attention_backward_dense,
-                       attention_backward_varlen)
+                       attention_backward_padded, attention_backward_varlen)
 from .padding import attention_padded
 from .tiled import attention_tiled
 
 __all__ = ["attention", "attention_probs", "attention_dense", "attention_varlen",
            "attention_tiled", "attention_backward", "attention_backward_dense",
-           "attention_backward_varlen", "attention_padded", "ORACLE_DTYPE"]
+           "attention_backward_varlen", "attention_backward_padded", "attention_padded",
+           "ORACLE_DTYPE"]

@@ -264,3 +264,68 @@ def test_lse_merge_of_key_chunks_is_attention():
         Om = sum(np.exp(p[1][0] - Lm) * p[0][0] for p in parts)
         np.testing.assert_allclose(Om, O[0], rtol=0, atol=1e-13)
         np.testing.assert_allclose(Lm, L[0], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Backward with a band and with a key padding mask
+# ---------------------------------------------------------------------------
+
+from oracle import attention_backward_padded  # noqa: E402
+
+
+def _fd_grads(loss, arrays, h=1e-6):
+    grads = []
+    for which in range(len(arrays)):
+        g = np.zeros_like(arrays[which])
+        for idx in np.ndindex(*g.shape):
+            plus = [a.copy() for a in arrays]
+            minus = [a.copy() for a in arrays]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            g[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("window", [(None, 0), (1, 0), (0, 2), (2, 1), (0, 0), (1, None)])
+@pytest.mark.parametrize("Nq,Nk", [(4, 4), (3, 6), (6, 3)])
+def test_backward_band_finite_differences(window, Nq, Nk):
+    """Gradients with a band against central differences of the (pinned) band
+    forward; rows that see no key have zero gradients."""
+    rng = np.random.default_rng(51 + Nq + 7 * Nk)
+    q, k, v = rng.standard_normal((Nq, 3)), rng.standard_normal((Nk, 3)), rng.standard_normal((Nk, 2))
+    do = rng.standard_normal((Nq, 2))
+
+    def loss(q_, k_, v_):
+        O, _ = attention(q_, k_, v_, 0.7, window=window)
+        return float(np.sum(O * do))
+    dq, dk, dv, delta = attention_backward(q, k, v, do, 0.7, window=window)
+    fq, fk, fv = _fd_grads(loss, [q, k, v])
+    np.testing.assert_allclose(dq, fq, atol=1e-7)
+    np.testing.assert_allclose(dk, fk, atol=1e-7)
+    np.testing.assert_allclose(dv, fv, atol=1e-7)
+    O, _ = attention(q, k, v, 0.7, window=window)
+    np.testing.assert_allclose(delta, np.sum(do * O, axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_padded_finite_differences(causal):
+    """Gradients with a key padding mask against central differences of the
+    (pinned) padded forward: zero at padding positions, and padding content
+    never matters."""
+    rng = np.random.default_rng(61 + causal)
+    B, S, H, d = 2, 6, 1, 2
+    q, k, v, do = (rng.standard_normal((B, S, H, d)) for _ in range(4))
+    mask = np.array([[1, 0, 1, 1, 0, 1], [1, 1, 1, 0, 0, 0]], dtype=np.uint8)
+
+    def loss(q_, k_, v_):
+        O, _ = attention_padded(q_, k_, v_, mask, 0.9, causal)
+        return float(np.sum(O * do))
+    dq, dk, dv, delta = attention_backward_padded(q, k, v, do, mask, 0.9, causal)
+    fq, fk, fv = _fd_grads(loss, [q, k, v])
+    np.testing.assert_allclose(dq, fq, atol=1e-7)
+    np.testing.assert_allclose(dk, fk, atol=1e-7)
+    np.testing.assert_allclose(dv, fv, atol=1e-7)
+    pad = mask == 0
+    assert np.all(dq[pad] == 0) and np.all(dk[pad] == 0) and np.all(dv[pad] == 0)
+    assert np.all(delta.transpose(0, 2, 1)[pad] == 0)
