@@ -42,7 +42,8 @@ import math
 
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
                    FA_ERR_UNSUPPORTED, FA_OK, FaError, check, decode_workspace_bytes, load,
-                   raw_fa_bwd, raw_fa_bwd_varlen, raw_fa_decode,
+                   raw_fa_bwd, raw_fa_bwd_band, raw_fa_bwd_padded, raw_fa_bwd_varlen,
+                   raw_fa_bwd_varlen_band, raw_fa_decode,
                    raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
                    raw_fa_fwd_varlen,
                    raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
@@ -222,8 +223,9 @@ def _check_contiguous(ts, names, dtype):
 
 
 def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None,
-           delta=None):
-    """Backward over an equal-length batch; returns (dq, dk, dv, delta)."""
+           delta=None, window=None, key_padding_mask=None):
+    """Backward over an equal-length batch; returns (dq, dk, dv, delta). window and
+    key_padding_mask are those of the forward call (fa_bwd_band, fa_bwd_padded)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check_tensor(t, n, 4)
@@ -244,17 +246,31 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=
     for t, n in ((lse, "lse"), (delta, "delta")):
         if t.shape != (B, H, Nq) or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous float32 tensor of shape (B, H, Nq)")
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+    dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        check(raw_fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                         delta.data_ptr(), B, Nq, Nk, H, d, _dtype_code(q.dtype),
-                         _scale(softmax_scale, d), int(bool(causal)), stream))
+        if key_padding_mask is not None:
+            m = key_padding_mask
+            if window is not None or Nk != Nq:
+                raise ValueError("key_padding_mask: self-attention only, and not with a window")
+            if not isinstance(m, torch.Tensor) or m.dtype not in (torch.bool, torch.uint8) \
+                    or tuple(m.shape) != (B, Nq) or m.device != q.device or not m.is_contiguous():
+                raise ValueError("key_padding_mask must be a contiguous (B, S) bool or uint8 "
+                                 "tensor on q's device")
+            check(raw_fa_bwd_padded(*ptrs, m.view(torch.uint8).data_ptr(), B, Nq, H, d, dt, scale,
+                                    int(bool(causal)), stream))
+        elif window is not None:
+            wl, wr = _window(window, causal)
+            check(raw_fa_bwd_band(*ptrs, B, Nq, Nk, H, d, dt, scale, wl, wr, stream))
+        else:
+            check(raw_fa_bwd(*ptrs, B, Nq, Nk, H, d, dt, scale, int(bool(causal)), stream))
     return dq, dk, dv, delta
 
 
 def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
-                  causal=False, dq=None, dk=None, dv=None, delta=None):
+                  causal=False, dq=None, dk=None, dv=None, delta=None, window=None):
     """Backward over a packed variable-length batch; returns (dq, dk, dv, delta)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
@@ -277,14 +293,18 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=N
     for t, n in ((lse, "lse"), (delta, "delta")):
         if t.shape != (H, total) or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous float32 tensor of shape (H, total)")
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens.data_ptr())
+    dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        check(raw_fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                dv.data_ptr(), delta.data_ptr(), cu_seqlens.data_ptr(),
-                                cu_seqlens.numel() - 1, int(max_seqlen), total, H, d,
-                                _dtype_code(q.dtype), _scale(softmax_scale, d),
-                                int(bool(causal)), stream))
+        if window is not None:
+            wl, wr = _window(window, causal)
+            check(raw_fa_bwd_varlen_band(*ptrs, cu_seqlens.numel() - 1, int(max_seqlen), total, H,
+                                         d, dt, scale, wl, wr, stream))
+        else:
+            check(raw_fa_bwd_varlen(*ptrs, cu_seqlens.numel() - 1, int(max_seqlen), total, H, d,
+                                    dt, scale, int(bool(causal)), stream))
     return dq, dk, dv, delta
 
 
@@ -293,19 +313,22 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, softmax_scale, causal):
+        def forward(ctx, q, k, v, softmax_scale, causal, window, key_padding_mask):
             q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-            o, lse = fa_fwd(q, k, v, softmax_scale=softmax_scale, causal=causal)
+            o, lse = fa_fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window=window,
+                            key_padding_mask=key_padding_mask)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.softmax_scale, ctx.causal = softmax_scale, causal
+            ctx.softmax_scale, ctx.causal, ctx.window = softmax_scale, causal, window
+            ctx.key_padding_mask = key_padding_mask
             return o
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, o, lse = ctx.saved_tensors
             dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, dout.contiguous(),
-                                   softmax_scale=ctx.softmax_scale, causal=ctx.causal)
-            return dq, dk, dv, None, None
+                                   softmax_scale=ctx.softmax_scale, causal=ctx.causal,
+                                   window=ctx.window, key_padding_mask=ctx.key_padding_mask)
+            return dq, dk, dv, None, None, None, None
 
     return _Attention
 
@@ -313,13 +336,14 @@ def _autograd_function():
 _ATTENTION_FN = None
 
 
-def attention(q, k, v, softmax_scale=None, causal=False):
+def attention(q, k, v, softmax_scale=None, causal=False, window=None, key_padding_mask=None):
     """o = softmax(scale q k^T) v over (B, N, H, d) tensors, differentiable: the
-    forward is fa_fwd and the backward fa_bwd (both HIP kernels)."""
+    forward is fa_fwd and the backward fa_bwd (both HIP kernels), with the same
+    causal flag, band or key padding mask."""
     global _ATTENTION_FN
     if _ATTENTION_FN is None:
         _ATTENTION_FN = _autograd_function()
-    return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal)
+    return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal, window, key_padding_mask)
 
 
 def fa_decode(q, k, v, seqlens_k=None, softmax_scale=None, out=None, lse=None, workspace=None):

@@ -18,7 +18,8 @@ FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
-            "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_decode",
+            "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_bwd_band",
+            "fa_bwd_varlen_band", "fa_bwd_padded", "fa_decode",
             "fa_decode_workspace_bytes", "fa_status_string",
             "fa_last_error", "fa_abi_version")
 
@@ -61,6 +62,12 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen_strided.restype = i32
     lib.fa_fwd_padded.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_padded.restype = i32
+    lib.fa_bwd_band.argtypes = [vp] * 10 + [i32] * 6 + [f32, i32, i32, vp]
+    lib.fa_bwd_band.restype = i32
+    lib.fa_bwd_varlen_band.argtypes = [vp] * 11 + [i32] * 6 + [f32, i32, i32, vp]
+    lib.fa_bwd_varlen_band.restype = i32
+    lib.fa_bwd_padded.argtypes = [vp] * 11 + [i32] * 5 + [f32, i32, vp]
+    lib.fa_bwd_padded.restype = i32
     lib.fa_decode.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
     lib.fa_decode.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -165,3 +172,25 @@ def raw_fa_decode(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, scale, workspa
 
 def decode_workspace_bytes(B, Nk, H, d) -> int:
     return int(load().fa_decode_workspace_bytes(B, Nk, H, d))
+
+
+def raw_fa_bwd_band(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype, scale,
+                    window_left, window_right, stream) -> int:
+    """Pointer-level call of fa_bwd_band; returns the status code."""
+    return load().fa_bwd_band(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype,
+                              scale, window_left, window_right, stream)
+
+
+def raw_fa_bwd_varlen_band(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs, max_seqlen,
+                           total, H, d, dtype, scale, window_left, window_right, stream) -> int:
+    """Pointer-level call of fa_bwd_varlen_band; returns the status code."""
+    return load().fa_bwd_varlen_band(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs,
+                                     max_seqlen, total, H, d, dtype, scale, window_left,
+                                     window_right, stream)
+
+
+def raw_fa_bwd_padded(q, k, v, o, dout, lse, dq, dk, dv, delta, mask, B, S, H, d, dtype, scale,
+                      causal, stream) -> int:
+    """Pointer-level call of fa_bwd_padded; returns the status code."""
+    return load().fa_bwd_padded(q, k, v, o, dout, lse, dq, dk, dv, delta, mask, B, S, H, d,
+                                dtype, scale, causal, stream)

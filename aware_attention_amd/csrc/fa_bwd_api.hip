@@ -1,5 +1,6 @@
-// C ABI of the backward pass (fa_bwd, fa_bwd_varlen): argument checks and
-// the three launches. The operation is documented in include/fa.h.
+// C ABI of the backward pass (fa_bwd, fa_bwd_varlen, and their band and
+// padding-mask forms): argument checks and the three launches. The operation
+// is documented in include/fa.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -16,44 +17,78 @@ using fa_host::aligned16;
 using fa_host::check_device;
 using fa_host::fail;
 
-template <int D, bool CAUSAL, bool VARLEN, bool F16>
+template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
 hipError_t launch_bwd_t(const fa::BwdParams& p, int64_t nrows, int N, uint32_t grid_k,
                         uint32_t grid_q, hipStream_t stream) {
   hipLaunchKernelGGL((fa::delta_kernel<D, F16>), dim3((uint32_t)((nrows + 255) / 256)), dim3(256),
                      0, stream, p.o, p.dout, p.delta, nrows, p.H, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16>), dim3(grid_k), dim3(fa::kBwdThreads),
-                     0, stream, p);
+  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM>), dim3(grid_k),
+                     dim3(fa::kBwdThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   fa::BwdParams pq = p;
   pq.n_tiles = (int32_t)(grid_q / (uint32_t)(p.H * p.nbatch));
-  hipLaunchKernelGGL((fa::dq_kernel<D, CAUSAL, VARLEN, F16>), dim3(grid_q), dim3(fa::kBwdThreads),
-                     0, stream, pq);
+  hipLaunchKernelGGL((fa::dq_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM>), dim3(grid_q),
+                     dim3(fa::kBwdThreads), 0, stream, pq);
   return hipGetLastError();
 }
 
-template <bool CAUSAL, bool VARLEN, bool F16>
+template <bool CAUSAL, bool VARLEN, bool F16, bool BAND, bool KPM>
 hipError_t launch_bwd_d(const fa::BwdParams& p, int d, int64_t nrows, int N, uint32_t grid_k,
                         uint32_t grid_q, hipStream_t stream) {
   switch (d) {
-    case 32: return launch_bwd_t<32, CAUSAL, VARLEN, F16>(p, nrows, N, grid_k, grid_q, stream);
-    case 64: return launch_bwd_t<64, CAUSAL, VARLEN, F16>(p, nrows, N, grid_k, grid_q, stream);
-    default: return launch_bwd_t<128, CAUSAL, VARLEN, F16>(p, nrows, N, grid_k, grid_q, stream);
+    case 32:
+      return launch_bwd_t<32, CAUSAL, VARLEN, F16, BAND, KPM>(p, nrows, N, grid_k, grid_q, stream);
+    case 64:
+      return launch_bwd_t<64, CAUSAL, VARLEN, F16, BAND, KPM>(p, nrows, N, grid_k, grid_q, stream);
+    default:
+      return launch_bwd_t<128, CAUSAL, VARLEN, F16, BAND, KPM>(p, nrows, N, grid_k, grid_q, stream);
+  }
+}
+
+// Mask of a backward launch: none, causal, a band (dense or varlen), or a key
+// padding mask (dense), alone or with causal.
+enum class BwdMask { kNone, kCausal, kBand, kPad, kPadCausal };
+
+template <bool VARLEN, bool F16>
+hipError_t launch_bwd_m(const fa::BwdParams& p, int d, BwdMask mask, int64_t nrows, int N,
+                        uint32_t grid_k, uint32_t grid_q, hipStream_t stream) {
+  switch (mask) {
+    case BwdMask::kCausal:
+      return launch_bwd_d<true, VARLEN, F16, false, false>(p, d, nrows, N, grid_k, grid_q, stream);
+    case BwdMask::kBand:
+      return launch_bwd_d<false, VARLEN, F16, true, false>(p, d, nrows, N, grid_k, grid_q, stream);
+    case BwdMask::kPad:
+    case BwdMask::kPadCausal:
+      if constexpr (!VARLEN) {
+        return mask == BwdMask::kPad
+                   ? launch_bwd_d<false, false, F16, false, true>(p, d, nrows, N, grid_k, grid_q, stream)
+                   : launch_bwd_d<true, false, F16, false, true>(p, d, nrows, N, grid_k, grid_q, stream);
+      }
+      return hipErrorInvalidValue;
+    default:
+      return launch_bwd_d<false, VARLEN, F16, false, false>(p, d, nrows, N, grid_k, grid_q, stream);
   }
 }
 
 template <bool VARLEN>
-hipError_t launch_bwd(const fa::BwdParams& p, int d, int32_t dtype, bool causal, int64_t nrows,
+hipError_t launch_bwd(const fa::BwdParams& p, int d, int32_t dtype, BwdMask mask, int64_t nrows,
                       int N, uint32_t grid_k, uint32_t grid_q, hipStream_t stream) {
-  const bool f16 = dtype == FA_DTYPE_F16;
-  if (causal)
-    return f16 ? launch_bwd_d<true, VARLEN, true>(p, d, nrows, N, grid_k, grid_q, stream)
-               : launch_bwd_d<true, VARLEN, false>(p, d, nrows, N, grid_k, grid_q, stream);
-  return f16 ? launch_bwd_d<false, VARLEN, true>(p, d, nrows, N, grid_k, grid_q, stream)
-             : launch_bwd_d<false, VARLEN, false>(p, d, nrows, N, grid_k, grid_q, stream);
+  return dtype == FA_DTYPE_F16
+             ? launch_bwd_m<VARLEN, true>(p, d, mask, nrows, N, grid_k, grid_q, stream)
+             : launch_bwd_m<VARLEN, false>(p, d, mask, nrows, N, grid_k, grid_q, stream);
 }
+
+// Window sides: >= 0, or -1 for unbounded (passed to the kernels as
+// max(nq, nk), which reaches every key); sequences up to 2^29 keep the
+// kernels' 32-bit band bounds in range.
+int32_t bwd_window_side(int32_t w, int64_t nq, int64_t nk) {
+  const int64_t unbounded = nq > nk ? nq : nk;
+  return (int32_t)((w < 0 || w > unbounded) ? unbounded : w);
+}
+constexpr int64_t kMaxBandLenBwd = int64_t{1} << 29;
 
 fa_status check_bwd_common(int32_t H, int32_t d, int32_t dtype, float scale, int32_t causal) {
   if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
@@ -76,15 +111,11 @@ bool all_aligned(const void* const* ptrs, int n) {
 
 constexpr float kLog2eHost = 1.44269504088896340736f;
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
-                 int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
-                 float softmax_scale, int32_t causal, void* stream) {
-  fa_host::g_last_error.clear();
+fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
+                    int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
+                    float softmax_scale, int32_t causal, BwdMask mask, int32_t win_left,
+                    int32_t win_right, const uint8_t* kpm, void* stream) {
   const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
   for (const void* x : ptrs)
     if (!x) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -92,6 +123,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   fa_status st = check_bwd_common(H, d, dtype, softmax_scale, causal);
   if (st != FA_OK) return st;
   if (causal && Nq != Nk) return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
+  if (mask == BwdMask::kBand && (Nq > kMaxBandLenBwd || Nk > kMaxBandLenBwd))
+    return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
   if (!all_aligned(ptrs, 10)) return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const int64_t units = (int64_t)H * B;
   const int64_t grid_k = (Nk + fa::kBwdRows - 1) / fa::kBwdRows * units;
@@ -126,24 +159,31 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.n_tiles = (int32_t)(grid_k / units);
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * kLog2eHost;
-  const hipError_t e = launch_bwd<false>(p, d, dtype, causal == 1, nrows, Nq, (uint32_t)grid_k,
+  p.win_left = bwd_window_side(win_left, Nq, Nk);
+  p.win_right = bwd_window_side(win_right, Nq, Nk);
+  p.band_off = Nk - Nq;
+  p.kpm = kpm;
+  p.kpm_batch_stride = Nk;
+  const hipError_t e = launch_bwd<false>(p, d, dtype, mask, nrows, Nq, (uint32_t)grid_k,
                                          (uint32_t)grid_q, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
 }
 
-fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
-                        int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
-                        float softmax_scale, int32_t causal, void* stream) {
-  fa_host::g_last_error.clear();
+fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                     int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
+                     float softmax_scale, int32_t causal, BwdMask mask, int32_t win_left,
+                     int32_t win_right, void* stream) {
   if (!cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
   if (num_seqs < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
   if (total < 0 || max_seqlen < 0) return fail(FA_ERR_INVALID_ARGUMENT, "total and max_seqlen must be >= 0");
   if (max_seqlen > total) return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen exceeds total");
   fa_status st = check_bwd_common(H, d, dtype, softmax_scale, causal);
   if (st != FA_OK) return st;
+  if (mask == BwdMask::kBand && max_seqlen > kMaxBandLenBwd)
+    return fail(FA_ERR_UNSUPPORTED, "banded attention supports max_seqlen <= 2^29");
   if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
   const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
   for (const void* x : ptrs)
@@ -183,10 +223,82 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   p.n_tiles = (int32_t)n_t;
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * kLog2eHost;
-  const hipError_t e = launch_bwd<true>(p, d, dtype, causal == 1, nrows, total, (uint32_t)grid,
+  p.win_left = bwd_window_side(win_left, max_seqlen, max_seqlen);
+  p.win_right = bwd_window_side(win_right, max_seqlen, max_seqlen);
+  p.band_off = 0;
+  const hipError_t e = launch_bwd<true>(p, d, dtype, mask, nrows, total, (uint32_t)grid,
                                         (uint32_t)grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
+}
+
+fa_status check_bwd_window(int32_t left, int32_t right) {
+  if (left < -1 || right < -1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window sides must be >= 0, or -1 for unbounded");
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
+                 int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
+                 float softmax_scale, int32_t causal, void* stream) {
+  fa_host::g_last_error.clear();
+  return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype, softmax_scale,
+                   causal, causal == 1 ? BwdMask::kCausal : BwdMask::kNone, -1, -1, nullptr, stream);
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
+                        float softmax_scale, int32_t causal, void* stream) {
+  fa_host::g_last_error.clear();
+  return varlen_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, cu_seqlens, num_seqs, max_seqlen,
+                    total, H, d, dtype, softmax_scale, causal,
+                    causal == 1 ? BwdMask::kCausal : BwdMask::kNone, -1, -1, stream);
+}
+
+fa_status fa_bwd_band(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                      int32_t dtype, float softmax_scale, int32_t window_left,
+                      int32_t window_right, void* stream) {
+  fa_host::g_last_error.clear();
+  const fa_status st = check_bwd_window(window_left, window_right);
+  if (st != FA_OK) return st;
+  return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype, softmax_scale,
+                   0, BwdMask::kBand, window_left, window_right, nullptr, stream);
+}
+
+fa_status fa_bwd_varlen_band(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                             int32_t max_seqlen, int32_t total, int32_t H, int32_t d,
+                             int32_t dtype, float softmax_scale, int32_t window_left,
+                             int32_t window_right, void* stream) {
+  fa_host::g_last_error.clear();
+  const fa_status st = check_bwd_window(window_left, window_right);
+  if (st != FA_OK) return st;
+  return varlen_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, cu_seqlens, num_seqs, max_seqlen,
+                    total, H, d, dtype, softmax_scale, 0, BwdMask::kBand, window_left,
+                    window_right, stream);
+}
+
+fa_status fa_bwd_padded(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, const uint8_t* key_padding_mask, int32_t B, int32_t S,
+                        int32_t H, int32_t d, int32_t dtype, float softmax_scale, int32_t causal,
+                        void* stream) {
+  fa_host::g_last_error.clear();
+  if (!key_padding_mask) return fail(FA_ERR_INVALID_ARGUMENT, "null key_padding_mask");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, S, S, H, d, dtype, softmax_scale,
+                   causal, causal ? BwdMask::kPadCausal : BwdMask::kPad, -1, -1, key_padding_mask,
+                   stream);
 }
 
 }  // extern "C"

@@ -57,6 +57,13 @@ struct BwdParams {
   int32_t n_tiles;             // 128-row tiles per unit in this launch
   float scale;                 // softmax scale
   float scale_log2;            // scale * log2(e)
+  // Banded mask (BAND instances): query i sees key j iff
+  // i + band_off - win_left <= j <= i + band_off + win_right.
+  int32_t win_left, win_right, band_off;
+  // Key padding mask (KPM instances, dense): token n of batch b is valid iff
+  // kpm[b * kpm_batch_stride + n] != 0.
+  const uint8_t* kpm;
+  int64_t kpm_batch_stride;
 };
 
 constexpr int kBwdWaves = 4;
@@ -152,6 +159,21 @@ __device__ __forceinline__ bf16x8 lds_tr8(const uint8_t* smem, int byte, int byt
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// A lane's 32 keys of a 64-key tile are the 4-key groups 8 g + 4 (l/32) + 0..3
+// (g = 0..7); given the tile's 64 validity bits (a ballot), gather the
+// lane's bits so that key 32 kb + 8 (r/4) + 4 (l/32) + r%4 of register r in
+// block kb lands at bit 16 kb + r (scalar code, once per tile).
+__device__ __forceinline__ uint32_t gather_lane_bits(uint64_t kbits, int hi) {
+  auto gather = [](uint64_t x) -> uint32_t {   // nibble 2n of x -> nibble n
+    x &= 0x0F0F0F0F0F0F0F0Full;
+    x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
+    x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
+    return (uint32_t)(x | (x >> 16));
+  };
+  const uint32_t even = gather(kbits), odd = gather(kbits >> 4);
+  return hi ? odd : even;
+}
+
 // Work item of a workgroup: (128-row tile, head, batch or sequence) with the
 // tile index taken from blockIdx.x / units; offsets of the unit's rows.
 struct BwdUnit {
@@ -200,10 +222,11 @@ __device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16 (&acc)[D 
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool F16>
+template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdParams p) {
+  static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = kBwdTile * RBP;
@@ -239,8 +262,22 @@ void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int b = 0; b < DB; ++b) dk[b] = dv[b] = f32x16{};
 
-  const int n_qt = (u.Nq + kBwdTile - 1) / kBwdTile;
-  const int qt0 = CAUSAL ? k0 / kBwdTile : 0;
+  int n_qt = (u.Nq + kBwdTile - 1) / kBwdTile;
+  int qt0 = CAUSAL ? k0 / kBwdTile : 0;
+  // Band: the queries that see some key of this workgroup, i in
+  // [k0 - band_hi, k0 + kBwdRows - 1 - band_lo].
+  const int band_lo = BAND ? p.band_off - p.win_left : 0;
+  const int band_hi = BAND ? p.band_off + p.win_right : 0;
+  if constexpr (BAND) {
+    const int q_lo = max(0, k0 - band_hi);
+    const int q_hi = min(u.Nq - 1, min(u.Nk, k0 + kBwdRows) - 1 - band_lo);
+    qt0 = q_lo / kBwdTile;
+    n_qt = q_hi >= q_lo ? q_hi / kBwdTile + 1 : qt0;
+  }
+  // Padding mask: this lane's key takes part only if it is a valid token;
+  // padding queries get L = +inf below, so their P is 0.
+  const uint8_t* kpm_row = KPM ? p.kpm + (int64_t)u.bidx * p.kpm_batch_stride : nullptr;
+  const bool k_valid = !KPM || (krow < u.Nk && kpm_row[krow] != 0);
   const bool wave_has = kw0 < u.Nk;
   // Copies of query tile qt into buffer b, and its L, D values into registers
   // (threads 0..63, one query each; padding queries get L = +inf, D = 0).
@@ -251,7 +288,8 @@ void dkdv_kernel(BwdParams p) {
   };
   auto load_ld = [&](int qt, float& lv, float& dv_) __attribute__((always_inline)) {
     const int qi = qt * kBwdTile + tid;
-    lv = qi < u.Nq ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
+    const bool qv = qi < u.Nq && (!KPM || kpm_row[qi] != 0);
+    lv = qv ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
     dv_ = qi < u.Nq ? p.delta[u.l_off + qi] : 0.f;
   };
   auto store_ld = [&](int b, float lv, float dv_) __attribute__((always_inline)) {
@@ -312,7 +350,9 @@ void dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * t + 4 * half + e;
-            const bool ok = !CAUSAL || krow <= qb0 + q4 + e;
+            const int qi = qb0 + q4 + e;
+            bool ok = (!CAUSAL || krow <= qi) && k_valid;
+            if constexpr (BAND) ok = ok && krow >= qi + band_lo && krow <= qi + band_hi;
             const float pe = ok ? __builtin_amdgcn_exp2f(s[qb][r] * p.scale_log2 - Lv[e]) : 0.f;
             pv[e] = pe;
             dsv[e] = pe * (dp[qb][r] - Dv[e]);
@@ -350,10 +390,11 @@ void dkdv_kernel(BwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool F16>
+template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void dq_kernel(BwdParams p) {
+  static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = kBwdTile * RBP;
@@ -380,7 +421,9 @@ void dq_kernel(BwdParams p) {
       qr[s] = __builtin_bit_cast(bf16x8, qs[2 * s + hi]);
       dor[s] = __builtin_bit_cast(bf16x8, os[2 * s + hi]);
     }
-    Lq = p.lse[u.l_off + qrow] * kLog2eF;
+    // A padding query (padding mask) gets L = +inf, so its P and dQ are 0.
+    const bool qv = !KPM || p.kpm[(int64_t)u.bidx * p.kpm_batch_stride + qrow] != 0;
+    Lq = qv ? p.lse[u.l_off + qrow] * kLog2eF : __builtin_inff();
     Dq = p.delta[u.l_off + qrow];
   } else {
 #pragma unroll
@@ -393,6 +436,17 @@ void dq_kernel(BwdParams p) {
 
   const int kend = CAUSAL ? min(u.Nk, q0 + kBwdRows) : u.Nk;
   const int n_kt = (kend + kBwdTile - 1) / kBwdTile;
+  // Key tiles [kt_begin, kt_stop) hold a key some row of the workgroup sees.
+  int kt_begin = 0, kt_stop = n_kt;
+  const int band_lo = BAND ? p.band_off - p.win_left : 0;
+  const int band_hi = BAND ? p.band_off + p.win_right : 0;
+  if constexpr (BAND) {
+    const int k_lo = max(0, q0 + band_lo);
+    const int k_hi = min(u.Nk - 1, min(u.Nq, q0 + kBwdRows) - 1 + band_hi);
+    kt_begin = k_lo / kBwdTile;
+    kt_stop = k_hi >= k_lo ? k_hi / kBwdTile + 1 : kt_begin;
+  }
+  const uint8_t* kpm_row = KPM ? p.kpm + (int64_t)u.bidx * p.kpm_batch_stride : nullptr;
   const bool wave_has = qw0 < u.Nq;
   const int wave_last_kt = CAUSAL ? (qw0 + 31) / kBwdTile : n_kt - 1;
   auto issue = [&](int kt, int b) __attribute__((always_inline)) {
@@ -400,16 +454,21 @@ void dq_kernel(BwdParams p) {
     copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.v + u.k_off, rs, kt * kBwdTile, u.Nk, wave,
                        lane);
   };
-  if (n_kt > 0) issue(0, 0);
+  if (kt_begin < kt_stop) issue(kt_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = kt_begin; kt < kt_stop; ++kt) {
     const int kb0 = kt * kBwdTile;
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);   // buffer last read before the previous barrier
+    const int buf = (kt - kt_begin) & 1;
+    if (kt + 1 < kt_stop) issue(kt + 1, buf ^ 1);   // buffer last read before the previous barrier
     const uint8_t* k_lds = smem + (2 * buf) * TB;
     const uint8_t* v_lds = smem + (2 * buf + 1) * TB;
     if (wave_has && kt <= wave_last_kt) {
+    uint32_t kvalid = ~0u;   // padding mask: validity bits of this lane's 32 keys
+    if constexpr (KPM) {
+      const int key = kb0 + lane;
+      kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(key < u.Nk && kpm_row[key] != 0), hi);
+    }
 
     // S^T = K Q^T and dP^T = V dO^T: this tile's 64 keys x the wave's 32 queries.
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -436,7 +495,9 @@ void dq_kernel(BwdParams p) {
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * t + 2 * i + e;
             const int key = kb0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool ok = key < u.Nk && (!CAUSAL || key <= qrow);
+            bool ok = key < u.Nk && (!CAUSAL || key <= qrow);
+            if constexpr (BAND) ok = ok && key >= qrow + band_lo && key <= qrow + band_hi;
+            if constexpr (KPM) ok = ok && ((kvalid >> (16 * kb + r)) & 1);
             const float pe = ok ? __builtin_amdgcn_exp2f(s[kb][r] * p.scale_log2 - Lq) : 0.f;
             v2[e] = pe * (dp[kb][r] - Dq);
           }

@@ -273,6 +273,39 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
 /* Workspace bytes fa_decode needs for these sizes (0 for sizes below 1). */
 size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d);
 
+/*
+ * Backward of the banded forward (fa_fwd_band / fa_fwd_varlen_band): the
+ * arguments of fa_bwd / fa_bwd_varlen with the causal flag replaced by the
+ * window of the forward call (sides >= 0, or -1 for unbounded). Rows that
+ * saw no key get zero gradients. Errors: as fa_bwd; a window side below -1
+ * is FA_ERR_INVALID_ARGUMENT; Nq or Nk (max_seqlen) above 2^29 is
+ * FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_bwd_band(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                      int32_t dtype, float softmax_scale, int32_t window_left,
+                      int32_t window_right, void* stream);
+fa_status fa_bwd_varlen_band(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                             int32_t max_seqlen, int32_t total, int32_t H, int32_t d,
+                             int32_t dtype, float softmax_scale, int32_t window_left,
+                             int32_t window_right, void* stream);
+
+/*
+ * Backward of the padded forward (fa_fwd_padded): tensors (B, S, H, d), lse and
+ * delta (B, H, S), the same key_padding_mask (DEVICE uint8 (B, S), nonzero =
+ * valid) and causal flag. The gradients are those of attention over the
+ * valid tokens; padding positions get zero dq, dk, dv. Errors: as fa_bwd; a
+ * null mask is FA_ERR_INVALID_ARGUMENT.
+ */
+fa_status fa_bwd_padded(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, const uint8_t* key_padding_mask, int32_t B, int32_t S,
+                        int32_t H, int32_t d, int32_t dtype, float softmax_scale, int32_t causal,
+                        void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int32_t status);
 

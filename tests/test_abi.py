@@ -418,3 +418,26 @@ def test_decode_valid_call_without_a_device_is_a_hip_error():
         pytest.skip("a GPU is present; this case covers hosts without one")
     assert _decode() == HIP
     assert _decode(d=256, sl=P, dtype=_lib.FA_DTYPE_F16) == HIP
+
+
+def test_bwd_band_and_padded_argument_checks():
+    _lib_or_skip()
+    lib = _lib
+    args = [P] * 10
+    # window side below -1, bad dtype, d unsupported, null mask, causal out of range
+    assert lib.raw_fa_bwd_band(*args, 1, 128, 128, 2, 64, lib.FA_DTYPE_BF16, 0.1, -2, 0, None) == INV
+    assert lib.raw_fa_bwd_band(*args, 1, 128, 128, 2, 48, lib.FA_DTYPE_BF16, 0.1, 4, 0, None) == UNS
+    assert lib.raw_fa_bwd_band(*args, 1, (1 << 29) + 1, 128, 2, 64, lib.FA_DTYPE_BF16, 0.1, 4, 0,
+                               None) == UNS
+    assert lib.raw_fa_bwd_varlen_band(*args, None, 2, 100, 150, 2, 64, lib.FA_DTYPE_BF16, 0.1, 3,
+                                      3, None) == INV
+    assert lib.raw_fa_bwd_padded(*args, None, 2, 100, 2, 64, lib.FA_DTYPE_BF16, 0.1, 0, None) == INV
+    assert lib.raw_fa_bwd_padded(*args, P, 2, 100, 2, 64, lib.FA_DTYPE_BF16, 0.1, 2, None) == INV
+    assert lib.raw_fa_bwd_padded(*args, P, 2, 100, 2, 64, 7, 0.1, 0, None) == INV
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert lib.raw_fa_bwd_band(*args, 1, 128, 96, 2, 64, lib.FA_DTYPE_F16, 0.1, -1, 0, None) == HIP
+        assert lib.raw_fa_bwd_varlen_band(*args, P, 2, 100, 150, 2, 32, lib.FA_DTYPE_BF16, 0.1, 8,
+                                          8, None) == HIP
+        assert lib.raw_fa_bwd_padded(*args, P, 2, 100, 2, 128, lib.FA_DTYPE_BF16, 0.1, 1,
+                                     None) == HIP

@@ -40,9 +40,10 @@ EPS_O = {"bf16": 2.0**-8, "f16": 2.0**-10}   # relative rounding of O, doubled
 EPS_O_HIP = 2.0**-6                          # O from the HIP forward
 
 
-def d_rounding_terms(qf, kf, vf, dof, scale, causal, eps):
+def d_rounding_terms(qf, kf, vf, dof, scale, causal, eps, window=None, P=None):
     """One head: the dq, dk and D bounds of the D-from-16-bit-O rounding (module docstring)."""
-    P = attention_probs(qf, kf, scale, causal)
+    if P is None:
+        P = attention_probs(qf, kf, scale, causal, window=window)
     O = P @ vf
     dD = eps * np.sum(np.abs(dof * O), axis=1)                       # (Nq,)
     tq = scale * dD[:, None] * (P @ np.abs(kf))                      # (Nq, d)
@@ -50,15 +51,23 @@ def d_rounding_terms(qf, kf, vf, dof, scale, causal, eps):
     return tq, tk, dD
 
 
-def dense_terms(qf, kf, vf, dof, scale, causal, eps):
-    """d_rounding_terms over (B, N, H, d) tensors: tq, tk in the tensors' layouts, dD (B, H, Nq)."""
+def dense_terms(qf, kf, vf, dof, scale, causal, eps, window=None, mask=None):
+    """d_rounding_terms over (B, N, H, d) tensors: tq, tk in the tensors' layouts, dD (B, H, Nq).
+    mask: key padding mask (B, S); P is then that of the valid tokens, zero elsewhere."""
     B, Nq, H, _ = qf.shape
     tq, tk = np.zeros_like(qf), np.zeros_like(kf)
     dD = np.zeros((B, H, Nq))
     for b in range(B):
         for h in range(H):
+            P = None
+            if mask is not None:
+                idx = np.nonzero(mask[b])[0]
+                P = np.zeros((Nq, kf.shape[1]))
+                if idx.size:
+                    P[np.ix_(idx, idx)] = attention_probs(qf[b, idx, h], kf[b, idx, h], scale, causal)
             tq[b, :, h], tk[b, :, h], dD[b, h] = d_rounding_terms(
-                qf[b, :, h], kf[b, :, h], vf[b, :, h], dof[b, :, h], scale, causal, eps)
+                qf[b, :, h], kf[b, :, h], vf[b, :, h], dof[b, :, h], scale, causal, eps,
+                window=window, P=P)
     return tq, tk, dD
 
 
@@ -255,3 +264,123 @@ def test_bwd_full_size_prefill_sampled():
     scale_ = dkf.abs().sum(dim=1)
     assert torch.isfinite(dkf).all() and torch.isfinite(dq.double()).all()
     assert bool((colsum <= 2e-2 * scale_ + 1e-3).all()), float((colsum / scale_).max())
+
+
+# ---------------------------------------------------------------------------
+# Backward of the banded and the padded forward
+# ---------------------------------------------------------------------------
+
+from oracle import attention_backward_padded, attention_padded  # noqa: E402
+
+
+def check_bwd_band(B, Nq, Nk, H, d, window, seed):
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    say(f"bwd band B={B} Nq={Nq} Nk={Nk} H={H} d={d} window={window} seed={seed}")
+    q, k, v = W.make_dense(B, Nq, H, d, seed, Nk=Nk)
+    do = W.make_dense(B, Nq, H, d, seed + 1)[0]
+    scale = 1 / np.sqrt(d)
+    qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
+    oref, lref = attention_dense(qf, kf, vf, scale, window=window)
+    dq, dk, dv, delta = aa.fa_bwd(to_dev(q), to_dev(k), to_dev(v), to_dev(_round(oref, "bf16")),
+                                  torch.from_numpy(lref.astype(np.float32)).cuda(), to_dev(do),
+                                  softmax_scale=scale, window=window)
+    torch.cuda.synchronize()
+    gq, gk, gv, gd = attention_backward_dense(qf, kf, vf, dof, scale, window=window)
+    tq, tk, dD = dense_terms(qf, kf, vf, dof, scale, False, EPS_O["bf16"], window=window)
+    what = f"band {window} Nq={Nq} Nk={Nk} d={d}"
+    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
+    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
+    assert_grad_close(_np(dv), gv, "dv " + what)
+    assert_grad_close(_np(delta), gd, "delta " + what, per_row=False, extra=dD)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", [(None, 0), (16, 16), (100, 3), (0, None), (0, 0)])
+@pytest.mark.parametrize("Nq,Nk", [(333, 333), (129, 300), (300, 129)])
+def test_bwd_band(d, window, Nq, Nk):
+    # (300, 129): off = -171, rows before it see no key with a bounded right side.
+    check_bwd_band(1, Nq, Nk, 2, d, window, seed=8800 + Nq + Nk + d)
+
+
+def test_bwd_band_long_rows():
+    check_bwd_band(1, 1000, 1000, 2, 128, (300, 40), seed=8850)
+
+
+def test_bwd_band_varlen():
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    lengths = [1, 127, 0, 300, 64]
+    window = (20, 5)
+    say(f"bwd band varlen lengths={lengths} window={window}")
+    q, k, v, cu = W.make_varlen(lengths, 2, 64, seed=8870)
+    do, _, _, _ = W.make_varlen(lengths, 2, 64, seed=8871)
+    scale = 1 / 8.0
+    qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
+    oref, lref = attention_varlen(qf, kf, vf, cu, scale, window=window)
+    dq, dk, dv, _ = aa.fa_bwd_varlen(to_dev(q), to_dev(k), to_dev(v), to_dev(_round(oref, "bf16")),
+                                     torch.from_numpy(lref.astype(np.float32)).cuda(), to_dev(do),
+                                     torch.from_numpy(cu).cuda(), max(lengths), softmax_scale=scale,
+                                     window=window)
+    torch.cuda.synchronize()
+    gq, gk, gv, _ = attention_backward_varlen(qf, kf, vf, dof, cu, scale, window=window)
+    tq, tk = np.zeros_like(qf), np.zeros_like(kf)
+    for s_ in range(len(lengths)):
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        for h in range(2):
+            if b > a:
+                tq[a:b, h], tk[a:b, h], _ = d_rounding_terms(
+                    qf[a:b, h], kf[a:b, h], vf[a:b, h], dof[a:b, h], scale, False, EPS_O["bf16"],
+                    window=window)
+    assert_grad_close(_np(dq), gq, "band varlen dq", extra=tq)
+    assert_grad_close(_np(dk), gk, "band varlen dk", extra=tk)
+    assert_grad_close(_np(dv), gv, "band varlen dv")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_padded(d, causal):
+    import aware_attention_amd as aa
+    from tests.test_gpu_padded import _masks
+    torch = torch_or_skip()
+    B, S, H = 5, 333, 2
+    say(f"bwd padded B={B} S={S} d={d} causal={causal}")
+    q, k, v = W.make_dense(B, S, H, d, seed=8900 + d)
+    do = W.make_dense(B, S, H, d, seed=8901 + d)[0]
+    mask = _masks(B, S, 8900 + d)
+    scale = 1 / np.sqrt(d)
+    qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
+    oref, lref = attention_padded(qf, kf, vf, mask, scale, causal)
+    dq, dk, dv, delta = aa.fa_bwd(to_dev(q), to_dev(k), to_dev(v), to_dev(_round(oref, "bf16")),
+                                  torch.from_numpy(lref.astype(np.float32)).cuda(), to_dev(do),
+                                  softmax_scale=scale, causal=causal,
+                                  key_padding_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    gq, gk, gv, gd = attention_backward_padded(qf, kf, vf, dof, mask, scale, causal)
+    tq, tk, dD = dense_terms(qf, kf, vf, dof, scale, causal, EPS_O["bf16"], mask=mask)
+    what = f"padded d={d} causal={causal}"
+    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
+    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
+    assert_grad_close(_np(dv), gv, "dv " + what)
+    pad = mask == 0
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert np.all(_np(t)[pad] == 0), f"{n} must be 0 at padding positions"
+
+
+def test_autograd_with_band_and_padding_mask():
+    """The autograd wrapper passes the band and the padding mask to both passes
+    (bitwise equal to the direct calls)."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    say("autograd with band and padding mask")
+    q, k, v = (to_dev(x) for x in W.make_dense(2, 300, 2, 64, seed=8950))
+    do = to_dev(W.make_dense(2, 300, 2, 64, seed=8951)[0])
+    mask = torch.from_numpy(np.array([[1] * 200 + [0] * 100, [1] * 300], dtype=np.uint8)).cuda()
+    for kw in (dict(window=(30, 0)), dict(key_padding_mask=mask, causal=True)):
+        o, lse = aa.fa_fwd(q, k, v, **kw)
+        g = aa.fa_bwd(q, k, v, o, lse, do, **kw)
+        qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+        aa.attention(qa, ka, va, **kw).backward(do)
+        torch.cuda.synchronize()
+        for a, b_ in zip((qa.grad, ka.grad, va.grad), g[:3]):
+            assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), str(kw.keys())
