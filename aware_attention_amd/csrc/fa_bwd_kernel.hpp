@@ -222,6 +222,49 @@ __device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16 (&acc)[D 
   }
 }
 
+// Span of the valid tokens of one row of a key padding mask: lo and hi are the
+// first and last valid positions (lo > hi when the row has none), run says
+// that every position in [lo, hi] is valid. One pass over the row by the
+// whole workgroup; red is LDS for 3 ints per wave, free until the barrier
+// at the end.
+struct KpmSpan {
+  int lo, hi;
+  bool run;
+};
+__device__ __forceinline__ KpmSpan kpm_span(const uint8_t* row, int n, int* red, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int lo = n, hi = -1, cnt = 0;
+  for (int i = tid; i < n; i += kBwdThreads) {
+    if (row[i] != 0) {
+      lo = min(lo, i);
+      hi = max(hi, i);
+      ++cnt;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off, 64));
+    hi = max(hi, __shfl_xor(hi, off, 64));
+    cnt += __shfl_xor(cnt, off, 64);
+  }
+  if (lane == 0) {
+    red[3 * wave] = lo;
+    red[3 * wave + 1] = hi;
+    red[3 * wave + 2] = cnt;
+  }
+  __syncthreads();
+  lo = n;
+  hi = -1;
+  cnt = 0;
+#pragma unroll
+  for (int w = 0; w < kBwdWaves; ++w) {
+    lo = min(lo, red[3 * w]);
+    hi = max(hi, red[3 * w + 1]);
+    cnt += red[3 * w + 2];
+  }
+  __syncthreads();   // red may be overwritten after this
+  return {lo, hi, cnt == hi - lo + 1};
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(1, 1)))
@@ -275,10 +318,22 @@ void dkdv_kernel(BwdParams p) {
     n_qt = q_hi >= q_lo ? q_hi / kBwdTile + 1 : qt0;
   }
   // Padding mask: this lane's key takes part only if it is a valid token;
-  // padding queries get L = +inf below, so their P is 0.
+  // padding queries get L = +inf below, so their P is 0. Query tiles outside
+  // the span of valid tokens hold only padding and are skipped; a workgroup
+  // (or a wave) whose keys all lie outside it only writes zeros.
   const uint8_t* kpm_row = KPM ? p.kpm + (int64_t)u.bidx * p.kpm_batch_stride : nullptr;
   const bool k_valid = !KPM || (krow < u.Nk && kpm_row[krow] != 0);
-  const bool wave_has = kw0 < u.Nk;
+  KpmSpan span{0, u.Nk - 1, true};
+  if constexpr (KPM) {
+    span = kpm_span(kpm_row, u.Nk, reinterpret_cast<int*>(smem), tid);   // no tile copied yet
+    if (span.lo > span.hi || k0 > span.hi || k0 + kBwdRows - 1 < span.lo) {
+      n_qt = qt0;
+    } else {
+      qt0 = max(qt0, span.lo / kBwdTile);
+      n_qt = min(n_qt, span.hi / kBwdTile + 1);
+    }
+  }
+  const bool wave_has = kw0 < u.Nk && (!KPM || (kw0 <= span.hi && kw0 + 31 >= span.lo));
   // Copies of query tile qt into buffer b, and its L, D values into registers
   // (threads 0..63, one query each; padding queries get L = +inf, D = 0).
   auto issue = [&](int qt, int b) __attribute__((always_inline)) {
@@ -446,8 +501,22 @@ void dq_kernel(BwdParams p) {
     kt_begin = k_lo / kBwdTile;
     kt_stop = k_hi >= k_lo ? k_hi / kBwdTile + 1 : kt_begin;
   }
+  // Padding mask: key tiles outside the span of valid tokens hold only
+  // padding and are skipped; a workgroup (or a wave) whose queries all lie
+  // outside it only writes zeros. Inside the span, a key's validity comes from
+  // the span itself when the valid tokens form one run, else from the mask.
   const uint8_t* kpm_row = KPM ? p.kpm + (int64_t)u.bidx * p.kpm_batch_stride : nullptr;
-  const bool wave_has = qw0 < u.Nq;
+  KpmSpan span{0, u.Nk - 1, true};
+  if constexpr (KPM) {
+    span = kpm_span(kpm_row, u.Nk, reinterpret_cast<int*>(smem), tid);   // no tile copied yet
+    if (span.lo > span.hi || q0 > span.hi || q0 + kBwdRows - 1 < span.lo) {
+      kt_stop = kt_begin;
+    } else {
+      kt_begin = max(kt_begin, span.lo / kBwdTile);
+      kt_stop = min(kt_stop, span.hi / kBwdTile + 1);
+    }
+  }
+  const bool wave_has = qw0 < u.Nq && (!KPM || (qw0 <= span.hi && qw0 + 31 >= span.lo));
   const int wave_last_kt = CAUSAL ? (qw0 + 31) / kBwdTile : n_kt - 1;
   auto issue = [&](int kt, int b) __attribute__((always_inline)) {
     copy_tile_async<D>(smem_lds + (2 * b) * TB, p.k + u.k_off, rs, kt * kBwdTile, u.Nk, wave, lane);
@@ -467,7 +536,8 @@ void dq_kernel(BwdParams p) {
     uint32_t kvalid = ~0u;   // padding mask: validity bits of this lane's 32 keys
     if constexpr (KPM) {
       const int key = kb0 + lane;
-      kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(key < u.Nk && kpm_row[key] != 0), hi);
+      const bool kv = span.run ? (key >= span.lo && key <= span.hi) : (key < u.Nk && kpm_row[key] != 0);
+      kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(kv), hi);
     }
 
     // S^T = K Q^T and dP^T = V dO^T: this tile's 64 keys x the wave's 32 queries.

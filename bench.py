@@ -129,9 +129,15 @@ def cpu_baseline_bwd(wl: dict, budget_s: float = 12.0):
     for b in range(spec.B):
         for h in range(spec.H):
             f64 = lambda x: W.bf16_bits_to_f32(x[b, :, h]).astype(np.float64)  # noqa: E731
-            attention_backward(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), f64(do), spec.scale,
-                               spec.causal)
-            flops += per_head
+            if "mask" in wl:   # padded batch: the valid tokens of row b (right padding)
+                n = int(wl["mask"][b].sum())
+                attention_backward(f64(wl["q"])[:n], f64(wl["k"])[:n], f64(wl["v"])[:n],
+                                   f64(do)[:n], spec.scale, spec.causal)
+                flops += 2.5 * 4.0 * n * n * spec.d / (2 if spec.causal else 1)
+            else:
+                attention_backward(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), f64(do), spec.scale,
+                                   spec.causal, window=spec.window)
+                flops += per_head
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -240,9 +246,6 @@ def main():
                       window=spec.window, key_padding_mask=kpm)
 
         if args.backward:
-            if spec.window is not None or kpm is not None:
-                print("the backward takes no window or padding mask", file=sys.stderr)
-                sys.exit(2)
             step()
             do = to_dev(W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0])
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -251,7 +254,8 @@ def main():
 
             def step():  # noqa: F811 - the timed step is the backward
                 aa.fa_bwd(q, k, v, o, lse, do, softmax_scale=spec.scale, causal=spec.causal,
-                          dq=dq, dk=dk, dv=dv, delta=delta)
+                          dq=dq, dk=dk, dv=dv, delta=delta, window=spec.window,
+                          key_padding_mask=kpm)
     else:
         if args.backward:
             print("--backward is measured on equal-length workloads", file=sys.stderr)

@@ -337,17 +337,20 @@ def test_bwd_band_varlen():
     assert_grad_close(_np(dv), gv, "band varlen dv")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d,S", [(64, 333), (128, 333), (128, 1025)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_padded(d, causal):
+def test_bwd_padded(d, S, causal):
+    # Masks: right padding, scattered holes, all valid, all padding, a middle
+    # run (one batch row each); at S = 1025 whole workgroups lie outside the
+    # span of valid tokens.
     import aware_attention_amd as aa
     from tests.test_gpu_padded import _masks
     torch = torch_or_skip()
-    B, S, H = 5, 333, 2
+    B, H = 5, 2
     say(f"bwd padded B={B} S={S} d={d} causal={causal}")
-    q, k, v = W.make_dense(B, S, H, d, seed=8900 + d)
-    do = W.make_dense(B, S, H, d, seed=8901 + d)[0]
-    mask = _masks(B, S, 8900 + d)
+    q, k, v = W.make_dense(B, S, H, d, seed=8900 + d + S)
+    do = W.make_dense(B, S, H, d, seed=8901 + d + S)[0]
+    mask = _masks(B, S, 8900 + d + S)
     scale = 1 / np.sqrt(d)
     qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
     oref, lref = attention_padded(qf, kf, vf, mask, scale, causal)
