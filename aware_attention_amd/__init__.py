@@ -43,12 +43,13 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
                    FA_ERR_UNSUPPORTED, FA_OK, FaError, check, decode_workspace_bytes, load,
                    raw_fa_bwd, raw_fa_bwd_band, raw_fa_bwd_padded, raw_fa_bwd_varlen,
-                   raw_fa_bwd_varlen_band, raw_fa_decode,
+                   raw_fa_bwd_varlen_band, raw_fa_decode, raw_fa_fwd_local,
                    raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
                    raw_fa_fwd_varlen,
                    raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
 
-__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_decode", "attention",
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_fwd_local", "fa_bwd", "fa_bwd_varlen", "fa_decode",
+           "attention",
            "FaError", "load",
            "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
 
@@ -344,6 +345,42 @@ def attention(q, k, v, softmax_scale=None, causal=False, window=None, key_paddin
     if _ATTENTION_FN is None:
         _ATTENTION_FN = _autograd_function()
     return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal, window, key_padding_mask)
+
+
+def fa_fwd_local(q, k, v, n_global, map_w, window, softmax_scale=None, causal=False, out=None,
+                 lse=None):
+    """Local window on a token map plus global anchors: q, k, v (B, N, H, d) contiguous
+    bf16 or fp16; tokens [0, n_global) are anchors, the rest a row-major map of map_w
+    tokens per row; window = (win_rows, win_cols), e.g. (2, 2) for a 5 x 5 window.
+    Query i sees key j iff i or j is an anchor or their map positions are within the
+    window (and j <= i when causal). Returns (o (B, N, H, d), lse (B, H, N) float32)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, 4)
+    B, N, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one shape (B, N, H, d): q {tuple(q.shape)} "
+                         f"k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if not all(t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k and v must be contiguous")
+    win_rows, win_cols = (int(w) for w in window)
+    out = _out(out, q, (B, N, H, d), "out")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, N)")
+    clamp = lambda x: max(min(int(x), 2**31 - 1), -1)  # noqa: E731 - sizes beyond int32 mean no bound
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        check(raw_fa_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, N, H, d, _dtype_code(q.dtype),
+                               _scale(softmax_scale, d), int(bool(causal)), clamp(n_global),
+                               clamp(map_w), clamp(win_rows), clamp(win_cols), stream))
+    return out, lse
 
 
 def fa_decode(q, k, v, seqlens_k=None, softmax_scale=None, out=None, lse=None, workspace=None):

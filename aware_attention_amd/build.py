@@ -23,7 +23,7 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17",
 
 # Translation units of libfa.so: the forward entry points and host helpers,
 # the backward entry points and the decode. They compile in parallel, then link.
-SOURCES = ["fa_api.hip", "fa_bwd_api.hip", "fa_decode_api.hip"]
+SOURCES = ["fa_api.hip", "fa_bwd_api.hip", "fa_decode_api.hip", "fa_local_api.hip"]
 _NOISE = "is not a recognized feature for this target"
 
 

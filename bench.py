@@ -88,6 +88,11 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0):
                 attention(f64(wl["q"])[:n], f64(wl["k"])[:n], f64(wl["v"])[:n], spec.scale,
                           spec.causal)
                 flops += 4.0 * n * n * spec.d / (2 if spec.causal else 1)
+            elif spec.local is not None:   # anchors + local window on the token map
+                from oracle import attention_local
+                attention_local(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale,
+                                *spec.local, spec.causal)
+                flops += per_head
             else:
                 attention(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), spec.scale, spec.causal,
                           window=spec.window)
@@ -245,6 +250,17 @@ def main():
             aa.fa_fwd(q, k, v, softmax_scale=spec.scale, causal=spec.causal, out=o, lse=lse,
                       window=spec.window, key_padding_mask=kpm)
 
+        if spec.local is not None:
+            G, map_w, wr, wc = spec.local
+            config["local"] = {"n_global": G, "map_w": map_w, "window": [wr, wc]}
+
+            def step():  # noqa: F811 - the local-window entry point
+                aa.fa_fwd_local(q, k, v, G, map_w, (wr, wc), softmax_scale=spec.scale,
+                                causal=spec.causal, out=o, lse=lse)
+
+        if args.backward and spec.local is not None:
+            print("the local-window pattern has no backward", file=sys.stderr)
+            sys.exit(2)
         if args.backward:
             step()
             do = to_dev(W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0])

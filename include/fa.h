@@ -274,6 +274,34 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
 size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d);
 
 /*
+ * Local window on a token map plus global anchor tokens (self-attention):
+ * the detector's mix of local-window attention and a few global tokens
+ * ("YOLOv12官版镜像集成Flash Attention v2，提速原理浅析", section 4.2, dynamic
+ * sparse attention; the map of section 4.1). Tokens [0, n_global) are the
+ * anchors; tokens n_global.. form a row-major map of map_w tokens per row
+ * (token t at row (t - n_global) / map_w, column (t - n_global) % map_w; the
+ * last row may be short). Query i sees key j iff
+ *     i < n_global  or  j < n_global  or
+ *     |row_i - row_j| <= win_rows and |col_i - col_j| <= win_cols,
+ * and, when causal = 1, j <= i. So every query sees the anchors and an
+ * anchor query sees every key; a 5 x 5 window is win_rows = win_cols = 2.
+ * Only the anchor key tiles and the key tiles of the map rows in reach are
+ * read; every row sees at least itself, so no row is empty.
+ *   q, k, v, o  : (B, N, H, d) dtype, densely packed; o written
+ *   lse         : (B, H, N) float32, written
+ *   dtype       : FA_DTYPE_BF16 or FA_DTYPE_F16; d: 32, 64, 128 or 256
+ *   n_global >= 0 (values above N mean every token is an anchor),
+ *   map_w >= 1, win_rows >= 0, win_cols >= 0 (values beyond the map's
+ *   extent mean no bound).
+ * Errors: a negative pattern size or map_w < 1 is FA_ERR_INVALID_ARGUMENT;
+ * N above 2^28 or H*d above 2^24 is FA_ERR_UNSUPPORTED; otherwise as fa_fwd.
+ */
+fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int32_t B, int32_t N, int32_t H, int32_t d, int32_t dtype,
+                       float softmax_scale, int32_t causal, int32_t n_global, int32_t map_w,
+                       int32_t win_rows, int32_t win_cols, void* stream);
+
+/*
  * Backward of the banded forward (fa_fwd_band / fa_fwd_varlen_band): the
  * arguments of fa_bwd / fa_bwd_varlen with the causal flag replaced by the
  * window of the forward call (sides >= 0, or -1 for unbounded). Rows that

@@ -441,3 +441,30 @@ def test_bwd_band_and_padded_argument_checks():
                                           8, None) == HIP
         assert lib.raw_fa_bwd_padded(*args, P, 2, 100, 2, 128, lib.FA_DTYPE_BF16, 0.1, 1,
                                      None) == HIP
+
+
+def test_local_argument_checks():
+    _lib_or_skip()
+    lib = _lib
+    args = [P] * 5
+    bf = lib.FA_DTYPE_BF16
+    # null pointer, N < 1, causal out of range, bad dtype, negative scale, negative or
+    # zero pattern sizes, unsupported d, N above 2^28
+    assert lib.raw_fa_fwd_local(None, P, P, P, P, 1, 100, 2, 64, bf, 0.1, 0, 4, 10, 2, 2,
+                                None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 0, 2, 64, bf, 0.1, 0, 4, 10, 2, 2, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, bf, 0.1, 2, 4, 10, 2, 2, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, 9, 0.1, 0, 4, 10, 2, 2, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, bf, -0.1, 0, 4, 10, 2, 2, None) == UNS
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, -1, 10, 2, 2, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 0, 2, 2, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 10, -1, 2, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 10, 2, -3, None) == INV
+    assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 48, bf, 0.1, 0, 4, 10, 2, 2, None) == UNS
+    assert lib.raw_fa_fwd_local(*args, 1, (1 << 28) + 1, 2, 64, bf, 0.1, 0, 4, 10, 2, 2,
+                                None) == UNS
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():   # every check passed: the device lookup fails
+        assert lib.raw_fa_fwd_local(*args, 2, 1608, 4, 32, bf, 0.1, 1, 8, 40, 2, 2, None) == HIP
+        assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 256, lib.FA_DTYPE_F16, 0.0, 0, 1000, 1, 0,
+                                    0, None) == HIP

@@ -131,3 +131,10 @@ def test_decode_workload_recipe():
     rng = np.random.default_rng(spec.seed)
     q = W.f32_to_bf16_bits(rng.standard_normal((16, 1, 32, 128), dtype=np.float32))
     assert np.array_equal(q, wl["q"])
+
+
+def test_local_pair_count_matches_the_oracle_mask():
+    from oracle import local_pairs
+    for args in [(1608, 8, 40, 2, 2, False), (777, 3, 17, 3, 1, True), (300, 300, 5, 0, 0, True),
+                 (50, 0, 7, 1, 2, False), (129, 70, 13, 0, 0, True)]:
+        assert W.local_pairs_count(*args) == local_pairs(*args), args

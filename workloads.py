@@ -20,6 +20,8 @@ Workloads (shapes follow the pages' models):
   prefill8k_d256  B=1 H=16 N=8192 d=256 causal (prefill8k's FLOPs at head dim 256)  seed 7
   vitpad      the vit batch with a key padding mask: row b keeps its first
               n_b ~ U{256..1025} tokens (lengths seed 10), the rest is padding
+  detlocal    B=16 H=4 N=1608 d=32: 8 global anchor tokens + the 40x40 map,
+              5x5 local window (the detector's local + global mix)  seed 11
 
 The detector token counts (40x40, 20x20 and the 4-head, 32-wide head split)
 come from "YOLOv12官版镜像集成Flash Attention v2，提速原理浅析" (sections 2.1 and
@@ -93,6 +95,8 @@ class Dense:
     window: tuple | None = None   # banded mask (left, right), None = unbounded side
     pad_seed: int | None = None   # key padding mask: right padding to lengths
                                   # drawn U{256..N} with this seed
+    local: tuple | None = None    # (n_global, map_w, win_rows, win_cols): anchors
+                                  # + a local window on the token map
 
     @property
     def scale(self) -> float:
@@ -112,6 +116,8 @@ class Dense:
             return f / 2 if self.causal else f
         if self.window is not None:
             return 4.0 * band_pairs(self.N, self.N, self.window) * self.d * self.H * self.B
+        if self.local is not None:
+            return 4.0 * local_pairs_count(self.N, *self.local, self.causal) * self.d * self.H * self.B
         f = 4.0 * self.N * self.N * self.d * self.H * self.B
         return f / 2 if self.causal else f
 
@@ -172,6 +178,8 @@ WORKLOADS = {
     "prefill2k": Dense("prefill2k", B=4, H=32, N=2048, d=128, causal=True, seed=55),
     "band8k": Dense("band8k", B=1, H=32, N=8192, d=128, causal=False, seed=6,
                     window=(2047, 0)),
+    "detlocal": Dense("detlocal", B=16, H=4, N=1608, d=32, causal=False, seed=11,
+                      local=(8, 40, 2, 2)),
     "prefill8k_d256": Dense("prefill8k_d256", B=1, H=16, N=8192, d=256, causal=True, seed=7),
     "decode8k": Decode("decode8k", B=16, H=32, Nk=8192, d=128, seed=8),
     "decode32k": Decode("decode32k", B=4, H=32, Nk=32768, d=128, seed=9),
@@ -189,6 +197,25 @@ def band_pairs(Nq: int, Nk: int, window) -> int:
     lo = np.zeros_like(i) if left is None else np.maximum(0, i - left)
     hi = np.full_like(i, Nk - 1) if right is None else np.minimum(Nk - 1, i + right)
     return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def local_pairs_count(N: int, n_global: int, map_w: int, win_rows: int, win_cols: int,
+                      causal: bool = False) -> int:
+    """Number of (query, key) pairs the local-window + anchor pattern leaves
+    visible, for FLOP accounting: an anchor query sees every key (up to itself
+    when causal); a map query sees the anchors and the map tokens within
+    (win_rows, win_cols) of its own map position."""
+    G = min(n_global, N)
+    t = np.arange(N, dtype=np.int64)
+    total = int(np.sum(t[:G] + 1)) if causal else G * N
+    m = np.arange(N - G, dtype=np.int64)
+    row, col = m // map_w, m % map_w
+    for i in range(N - G):
+        near = (np.abs(row - row[i]) <= win_rows) & (np.abs(col - col[i]) <= win_cols)
+        if causal:
+            near &= m <= i
+        total += G + int(np.count_nonzero(near))
+    return total
 
 
 def _draw(rng: np.random.Generator, shape) -> np.ndarray:
