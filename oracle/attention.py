@@ -38,7 +38,7 @@ Readings where the pages are silent:
     where off = Nk - Nq places the last query on the last key (so Nq == Nk
     gives off = 0) and None means no bound on that side. (None, 0) is causal
     attention with that alignment. A two-dimensional image window is not a
-    single band and is not covered.
+    single band; local.py covers it (with the page's global anchors).
   * A row that sees no key (possible only with a band) has the empty sum
     l = 0: its output is 0 and L = ln 0 = -inf.
 """
