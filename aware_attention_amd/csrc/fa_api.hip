@@ -103,12 +103,29 @@ hipError_t launch_t(const fa::FwdParams& p, int d, Mask mask, uint32_t grid, hip
 // Head dimension 256 (unmasked or causal): its own kernel, 128-row tiles.
 template <bool VARLEN, bool F16>
 hipError_t launch_256(const fa::FwdParams& p, Mask mask, uint32_t grid, hipStream_t stream) {
-  if (mask == Mask::kCausal)
-    hipLaunchKernelGGL((fa::fwd256_kernel<true, VARLEN, F16>), dim3(grid), dim3(fa::kBwdThreads),
-                       0, stream, p);
-  else
-    hipLaunchKernelGGL((fa::fwd256_kernel<false, VARLEN, F16>), dim3(grid), dim3(fa::kBwdThreads),
-                       0, stream, p);
+  const dim3 block(fa::kBwdThreads);
+  switch (mask) {
+    case Mask::kCausal:
+      hipLaunchKernelGGL((fa::fwd256_kernel<true, VARLEN, F16>), dim3(grid), block, 0, stream, p);
+      break;
+    case Mask::kBand:
+      hipLaunchKernelGGL((fa::fwd256_kernel<false, VARLEN, F16, true>), dim3(grid), block, 0,
+                         stream, p);
+      break;
+    case Mask::kPad:
+    case Mask::kPadCausal:
+      if constexpr (!VARLEN) {   // the padding mask is dense only (checked by the caller)
+        if (mask == Mask::kPad)
+          hipLaunchKernelGGL((fa::fwd256_kernel<false, false, F16, false, true>), dim3(grid), block,
+                             0, stream, p);
+        else
+          hipLaunchKernelGGL((fa::fwd256_kernel<true, false, F16, false, true>), dim3(grid), block,
+                             0, stream, p);
+      }
+      break;
+    default:
+      hipLaunchKernelGGL((fa::fwd256_kernel<false, VARLEN, F16>), dim3(grid), block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -190,11 +207,6 @@ fa_status check_common(int32_t H, int32_t d, float scale) {
 }
 
 // Head dimension 256 runs unmasked or causal only.
-fa_status check_d256(int32_t d, Mask mask) {
-  if (d == 256 && mask != Mask::kNone && mask != Mask::kCausal)
-    return fail(FA_ERR_UNSUPPORTED, "head dim 256 supports no band or padding mask");
-  return FA_OK;
-}
 
 void set_strides(fa::FwdParams& p, const Strides st[4]) {
   p.q_bs = st[0].b; p.q_ts = st[0].t; p.q_hs = st[0].h;
@@ -224,8 +236,6 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   }
   if ((mask == Mask::kCausal || mask == Mask::kPadCausal) && Nq != Nk)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
-  st_ = check_d256(d, mask);
-  if (st_ != FA_OK) return st_;
   if (mask == Mask::kBand && (Nq > kMaxBandLen || Nk > kMaxBandLen))
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -283,8 +293,6 @@ fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float
   }
   if (mask == Mask::kBand && max_seqlen > kMaxBandLen)
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports max_seqlen <= 2^29");
-  st_ = check_d256(d, mask);
-  if (st_ != FA_OK) return st_;
   if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||

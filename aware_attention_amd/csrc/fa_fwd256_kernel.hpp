@@ -17,7 +17,15 @@
 //     grows by more than kRescaleTau), P rounded to 16 bits in registers as
 //     the B operand of O^T += V^T P^T, whose A operand comes from transposing
 //     LDS reads of the V tile.
-// Masks: causal (tiles above a wave's diagonal skipped) and the sequence tail.
+// Masks: causal (tiles above a wave's diagonal skipped), the sequence tail,
+// the banded mask of fwd_kernel (BAND: query i sees key j iff
+// i + band_off - win_left <= j <= i + band_off + win_right; key tiles outside
+// the workgroup's band are not visited, a wave skips tiles outside its own)
+// and the key padding mask (KPM, dense: one pass over the batch row's mask
+// gives the span of valid tokens, tiles outside it are not visited, key
+// validity per tile comes from a ballot of the mask, or from the span when
+// the valid tokens form one run; padding queries get O = 0, L = -inf). A row
+// that sees no key gets O = 0 and L = -inf.
 #pragma once
 
 #include "fa_bwd_kernel.hpp"   // padded LDS tiles, async tile copies, operand lanes
@@ -26,10 +34,12 @@ namespace fa {
 
 constexpr int kRows256 = kBwdRows;   // query rows per workgroup (4 waves x 32)
 
-template <bool CAUSAL, bool VARLEN, bool F16>
+template <bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void fwd256_kernel(FwdParams p) {
+  static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
+  constexpr bool EMPTY_ROWS = BAND || KPM;
   constexpr int D = 256, DS = D / 16, DB = D / 32, BC = kBwdTile;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = BC * RBP;
@@ -89,24 +99,58 @@ void fwd256_kernel(FwdParams p) {
   float l_run = 0.f;       // running sum over this lane's half of the keys
 
   const int kend = CAUSAL ? min(Nk, q0 + kRows256) : Nk;
-  const int n_kt = (kend + BC - 1) / BC;
-  const bool wave_has = qw0 < Nq;
-  const int wave_last_kt = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BC) : n_kt - 1;
+  // Key tiles [kt_begin, kt_stop) hold a key some row of the workgroup sees.
+  int kt_begin = 0, kt_stop = (kend + BC - 1) / BC;
+  const int band_lo = BAND ? p.band_off - p.win_left : 0;
+  const int band_hi = BAND ? p.band_off + p.win_right : 0;
+  const int qw1 = min(Nq, qw0 + 32) - 1;   // last row of this wave
+  if constexpr (BAND) {
+    const int k_lo = max(0, q0 + band_lo);
+    const int k_hi = min(Nk - 1, min(Nq, q0 + kRows256) - 1 + band_hi);
+    kt_begin = k_lo / BC;
+    kt_stop = k_hi >= k_lo ? k_hi / BC + 1 : kt_begin;
+  }
+  const uint8_t* kpm_row = KPM ? p.kpm + (int64_t)bidx * p.kpm_batch_stride : nullptr;
+  KpmSpan span{0, Nk - 1, true};
+  if constexpr (KPM) {
+    span = kpm_span(kpm_row, Nk, reinterpret_cast<int*>(smem), tid);   // no tile copied yet
+    if (span.lo > span.hi || q0 > span.hi || q0 + kRows256 - 1 < span.lo) {
+      kt_stop = kt_begin;   // no valid key, or only padding queries
+    } else {
+      kt_begin = max(kt_begin, span.lo / BC);
+      kt_stop = min(kt_stop, span.hi / BC + 1);
+    }
+  }
+  const bool wave_has = qw0 < Nq && (!KPM || (qw0 <= span.hi && qw1 >= span.lo));
+  // This wave's last tile (causal) and, with a band, its first and last.
+  int wave_first_kt = kt_begin, wave_last_kt = kt_stop - 1;
+  if (CAUSAL) wave_last_kt = min(wave_last_kt, qw1 / BC);
+  if constexpr (BAND) {
+    wave_first_kt = max(wave_first_kt, max(0, qw0 + band_lo) / BC);
+    wave_last_kt = min(wave_last_kt, (qw1 + band_hi) / BC);
+  }
   auto issue = [&](int kt, int b) __attribute__((always_inline)) {
     copy_tile_async<D>(smem_lds + (2 * b) * TB, p.k + k_off, (int)p.k_ts, kt * BC, Nk, wave, lane);
     copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.v + v_off, (int)p.v_ts, kt * BC, Nk, wave,
                        lane);
   };
-  if (n_kt > 0) issue(0, 0);
+  if (kt_begin < kt_stop) issue(kt_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = kt_begin; kt < kt_stop; ++kt) {
     const int k0 = kt * BC;
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);   // buffer last read before the previous barrier
+    const int buf = (kt - kt_begin) & 1;
+    if (kt + 1 < kt_stop) issue(kt + 1, buf ^ 1);   // buffer last read before the previous barrier
     const uint8_t* k_lds = smem + (2 * buf) * TB;
     const uint8_t* v_lds = smem + (2 * buf + 1) * TB;
-    if (wave_has && kt <= wave_last_kt) {
+    if (wave_has && kt >= wave_first_kt && kt <= wave_last_kt) {
+      uint32_t kvalid = ~0u;   // padding mask: validity bits of this lane's 32 keys
+      if constexpr (KPM) {
+        const int key = k0 + lane;
+        const bool kv = span.run ? (key >= span.lo && key <= span.hi)
+                                 : (key < Nk && kpm_row[key] != 0);
+        kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(kv), hi);
+      }
       // S^T = K Q^T: 64 keys x the wave's 32 queries, keys in accumulator rows.
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -115,16 +159,20 @@ void fwd256_kernel(FwdParams p) {
         for (int kb = 0; kb < 2; ++kb)
           s[kb] = mfma32<F16>(lds16(k_lds, kb * 32 * RBP + ln.row_rd + ds * 32), qr[ds], s[kb]);
       }
-      // Online softmax (base 2); masked keys (past the end, or after the
-      // query when causal) get -inf, only on the tiles that can hold them.
-      const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0);
+      // Online softmax (base 2); masked keys (past the end, after the query
+      // when causal, outside the band, padding) get -inf, only on the tiles
+      // that can hold them.
+      const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0) || BAND || KPM;
       float mt = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = !masked || (key < Nk && (!CAUSAL || key <= qrow));
+          bool ok = (key < Nk) & (!CAUSAL | (key <= qrow));
+          if constexpr (BAND) ok = ok & (key >= qrow + band_lo) & (key <= qrow + band_hi);
+          if constexpr (KPM) ok = ok & (((kvalid >> (16 * kb + r)) & 1u) != 0);
+          ok = ok | !masked;
           s[kb][r] = ok ? s[kb][r] * s2 : kNegInf;
           mt = fmaxf(mt, s[kb][r]);
         }
@@ -133,12 +181,14 @@ void fwd256_kernel(FwdParams p) {
       if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
         asm volatile("" ::: "memory");   // keep the rescale a real branch
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // A row that has seen no key yet keeps m = -inf (no NaN from -inf - -inf).
+        const float alpha = (EMPTY_ROWS && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b) o[b] *= alpha;
         m_run = m_new;
       }
+      const float m_use = (EMPTY_ROWS && m_run == kNegInf) ? 0.f : m_run;   // no key yet: p = 0
       bf16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -148,8 +198,8 @@ void fwd256_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 8 * t + 2 * i;
-            const float e0 = __builtin_amdgcn_exp2f(s[kb][r] - m_run);
-            const float e1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - m_run);
+            const float e0 = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
+            const float e1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - m_use);
             w[i] = pack2<F16>(e0, e1);
             l_run += e0 + e1;
           }
@@ -171,11 +221,15 @@ void fwd256_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }
-  // Epilogue: O = O_acc / l, L = ln2 (m + log2 l).
+  // Epilogue: O = O_acc / l, L = ln2 (m + log2 l); a row that saw no key
+  // (band) or a padding query: O = 0, L = -inf.
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Nq) {
-    store_rowT<D, F16>(p.o + o_off + (int64_t)qrow * p.o_ts, o, __builtin_amdgcn_rcpf(l_tot), hi);
-    if (hi == 0) p.lse[l_off + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    bool empty = EMPTY_ROWS && !(l_tot > 0.f);
+    if constexpr (KPM) empty = empty || kpm_row[qrow] == 0;
+    store_rowT<D, F16>(p.o + o_off + (int64_t)qrow * p.o_ts, o,
+                       empty ? 0.f : __builtin_amdgcn_rcpf(l_tot), hi);
+    if (hi == 0) p.lse[l_off + qrow] = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 

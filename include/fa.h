@@ -27,7 +27,8 @@
  *     The library keeps no pointer after it returns and allocates no memory.
  *   - Q, K, V and O are bfloat16 (passed as void*), or fp16 where the
  *     *_strided entry points say so; L is float32.
- *   - Head dimension d must be 32, 64 or 128.
+ *   - Head dimension d must be 32, 64, 128 or 256 in the forward entry
+ *     points (every mask), 32, 64 or 128 in the backward.
  *   - softmax_scale must be finite and >= 0 (callers normally pass 1/sqrt(d)).
  *   - causal = 1 applies the lower-triangular mask of self-attention (query i
  *     sees keys j <= i) and needs as many queries as keys; causal = 0 is

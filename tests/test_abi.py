@@ -362,19 +362,21 @@ def test_padded_valid_call_without_a_device_is_a_hip_error():
 
 
 def test_head_dim_256_checks():
-    """d = 256 runs unmasked, causal and varlen; bands, padding masks and the
-    backward reject it on the host."""
+    """d = 256 runs every forward mask (unmasked, causal, varlen, bands,
+    padding masks); the backward rejects it on the host."""
     _lib_or_skip()
-    assert _band(d=256) == UNS
-    assert _padded(d=256) == UNS
-    assert _varlen_band(d=256) == UNS
     assert _bwd(d=256) == UNS
-    assert _strided(d=256, left=0, right=3) == UNS
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         return
     assert _fwd(d=256) == HIP and _fwd(d=256, causal=1) == HIP
     assert _varlen(d=256) == HIP
+    assert _band(d=256) == HIP
+    assert _padded(d=256) == HIP
+    assert _varlen_band(d=256) == HIP
+    assert _strided(d=256, left=0, right=3, qs=(100 * 3 * 256, 3 * 256, 256),
+                    ks=(80 * 3 * 256, 3 * 256, 256), vs=(80 * 3 * 256, 3 * 256, 256),
+                    os=(100 * 3 * 256, 3 * 256, 256)) == HIP
     assert _strided(d=256, qs=(100 * 3 * 256, 3 * 256, 256), ks=(80 * 3 * 256, 3 * 256, 256),
                     vs=(80 * 3 * 256, 3 * 256, 256), os=(100 * 3 * 256, 3 * 256, 256)) == HIP
 

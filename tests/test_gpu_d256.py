@@ -90,3 +90,63 @@ def test_d256_full_size_sampled():
         assert_l_close(lse[0, h, rows].cpu().numpy().astype(np.float64), lref[0, 0],
                        f"d256 full h={h}")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# Banded mask and key padding mask at head dimension 256
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [(None, 0), (0, 0), (16, 16), (100, 3), (0, None),
+                                    (63, 64), (None, None), (5, 200)])
+@pytest.mark.parametrize("Nq,Nk", [(333, 333), (129, 700), (700, 129)])
+def test_d256_band(window, Nq, Nk):
+    # (700, 129): off = -571, so with a bounded right side the first rows see no key.
+    from tests.test_gpu_band import check_band
+    check_band(2 if Nq == Nk else 1, Nq, Nk, 2, 256, window, seed=13000 + Nq + 3 * Nk)
+
+
+def test_d256_band_long_rows():
+    from tests.test_gpu_band import check_band
+    check_band(1, 1500, 1500, 2, 256, (700, 100), seed=13100)
+
+
+@pytest.mark.parametrize("window", [(None, 0), (7, 7), (0, 0), (200, None)])
+def test_d256_band_varlen(window):
+    import aware_attention_amd as aa
+    from tests.test_gpu_band import assert_l_band
+    torch = torch_or_skip()
+    lengths = [1, 127, 0, 128, 129, 300, 64]
+    say(f"d256 varlen band lengths={lengths} window={window}")
+    q, k, v, cu = W.make_varlen(lengths, 2, 256, seed=13200)
+    scale = 1 / 16.0
+    o, lse = aa.fa_fwd_varlen(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(cu).cuda(),
+                              max(lengths), softmax_scale=scale, window=window)
+    torch.cuda.synchronize()
+    oref, lref = attention_varlen(to_f64(q), to_f64(k), to_f64(v), cu, scale, window=window)
+    assert_o_close(o_to_f64(o), oref, f"d256 varlen window={window} O")
+    assert_l_band(lse.cpu().numpy().astype(np.float64), lref, f"d256 varlen window={window} L")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 65, 333])
+def test_d256_padded(causal, S):
+    # Five mask kinds (right padding, scattered holes, all valid, all padding,
+    # a middle run), one per batch row.
+    from tests.test_gpu_padded import check_padded
+    check_padded(5, S, 2, 256, causal, seed=13300 + S)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_padded_long_rows_with_empty_tiles(causal):
+    from tests.test_gpu_padded import check_padded
+    B, S = 3, 1100
+    m = np.ones((B, S), dtype=np.uint8)
+    m[0, :300] = 0
+    m[1, 600:] = 0
+    m[2, ::3] = 0
+    check_padded(B, S, 2, 256, causal, seed=13400, mask=m)
+
+
+def test_d256_padded_f16():
+    from tests.test_gpu_padded import check_padded
+    check_padded(5, 300, 2, 256, True, seed=13500, dtype="f16")

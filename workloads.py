@@ -20,6 +20,7 @@ Workloads (shapes follow the pages' models):
   prefill8k_d256  B=1 H=16 N=8192 d=256 causal (prefill8k's FLOPs at head dim 256)  seed 7
   vitpad      the vit batch with a key padding mask: row b keeps its first
               n_b ~ U{256..1025} tokens (lengths seed 10), the rest is padding
+  band8k_d256 B=1 H=16 N=8192 d=256 band (2047, 0)           seed 12
   detlocal    B=16 H=4 N=1608 d=32: 8 global anchor tokens + the 40x40 map,
               5x5 local window (the detector's local + global mix)  seed 11
 
@@ -180,6 +181,8 @@ WORKLOADS = {
                     window=(2047, 0)),
     "detlocal": Dense("detlocal", B=16, H=4, N=1608, d=32, causal=False, seed=11,
                       local=(8, 40, 2, 2)),
+    "band8k_d256": Dense("band8k_d256", B=1, H=16, N=8192, d=256, causal=False, seed=12,
+                         window=(2047, 0)),
     "prefill8k_d256": Dense("prefill8k_d256", B=1, H=16, N=8192, d=256, causal=True, seed=7),
     "decode8k": Decode("decode8k", B=16, H=32, Nk=8192, d=128, seed=8),
     "decode32k": Decode("decode32k", B=4, H=32, Nk=32768, d=128, seed=9),
