@@ -16,18 +16,21 @@ Contents:
   padding.py    attention over a padded batch with a key padding mask: remove
                 the padding, attend, put the result back (zeros at padding).
   local.py      attention with a local window on a token map plus global
-                anchor tokens, the score mask built from map coordinates.
+                anchor tokens, the score mask built from map coordinates, and
+                its gradients.
 """
 from .attention import (attention, attention_probs, attention_dense,
                         attention_varlen, ORACLE_DTYPE)
 from .backward import (attention_backward, attention_backward_dense,
                        attention_backward_padded, attention_backward_varlen)
-from .local import attention_local, attention_local_dense, local_pairs, local_visible
+from .local import (attention_local, attention_local_backward, attention_local_backward_dense,
+                    attention_local_dense, local_pairs, local_visible)
 from .padding import attention_padded
 from .tiled import attention_tiled
 
 __all__ = ["attention", "attention_probs", "attention_dense", "attention_varlen",
            "attention_tiled", "attention_backward", "attention_backward_dense",
            "attention_backward_varlen", "attention_backward_padded", "attention_padded",
-           "attention_local", "attention_local_dense", "local_pairs", "local_visible",
+           "attention_local", "attention_local_dense", "attention_local_backward",
+           "attention_local_backward_dense", "local_pairs", "local_visible",
            "ORACLE_DTYPE"]

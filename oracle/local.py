@@ -4,7 +4,8 @@ anchor tokens.
 TEST INFRASTRUCTURE ONLY (see the package docstring). Parity: pinned by the
 CPU tests (a pure-Python brute force that walks the map, reductions to the
 pinned banded and plain oracles, closed forms, a closed-form pair count,
-planted mistakes).
+planted mistakes; the gradients by central finite differences of the pinned
+forward and by the pinned banded backward).
 
 Sources (page titles and sections):
   * "YOLOv12官版镜像集成Flash Attention v2，提速原理浅析", section 4.2 (dynamic
@@ -97,3 +98,36 @@ def local_pairs(N: int, n_global: int, map_w: int, win_rows: int, win_cols: int,
                 causal: bool = False) -> int:
     """Number of visible (query, key) pairs (for FLOP counts)."""
     return int(np.count_nonzero(local_visible(N, n_global, map_w, win_rows, win_cols, causal)))
+
+
+def attention_local_backward(q, k, v, do, scale: float, n_global: int, map_w: int,
+                             win_rows: int, win_cols: int, causal: bool = False):
+    """One head: gradients of attention_local for a loss with dL/dO = do, by the
+    chain rule through the definition (as in backward.py: dV = P^T dO,
+    dS = P (dO V^T - D), D_i = sum_j P_ij (dO V^T)_ij, dQ = scale dS K,
+    dK = scale dS^T Q) with P the local pattern's probabilities.
+    Returns (dq, dk, dv, delta), float64."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    N = q.shape[0]
+    S = scale * (q @ k.T)
+    S = np.where(local_visible(N, n_global, map_w, win_rows, win_cols, causal), S, -np.inf)
+    e = np.exp(S - np.max(S, axis=1, keepdims=True))
+    P = e / np.sum(e, axis=1, keepdims=True)
+    dP = do @ v.T
+    delta = np.sum(P * dP, axis=1)
+    dS = P * (dP - delta[:, None])
+    return scale * (dS @ k), scale * (dS.T @ q), P.T @ do, delta
+
+
+def attention_local_backward_dense(q, k, v, do, scale: float, n_global: int, map_w: int,
+                                   win_rows: int, win_cols: int, causal: bool = False):
+    """(B, N, H, d) tensors -> dq, dk, dv in the input layouts and delta (B, H, N)."""
+    B, N, H, _ = q.shape
+    dq, dk, dv = (np.zeros(x.shape, dtype=ORACLE_DTYPE) for x in (q, k, v))
+    delta = np.zeros((B, H, N), dtype=ORACLE_DTYPE)
+    for b in range(B):
+        for h in range(H):
+            dq[b, :, h], dk[b, :, h], dv[b, :, h], delta[b, h] = attention_local_backward(
+                q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, n_global, map_w,
+                win_rows, win_cols, causal)
+    return dq, dk, dv, delta

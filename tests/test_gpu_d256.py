@@ -150,3 +150,34 @@ def test_d256_padded_long_rows_with_empty_tiles(causal):
 def test_d256_padded_f16():
     from tests.test_gpu_padded import check_padded
     check_padded(5, 300, 2, 256, True, seed=13500, dtype="f16")
+
+
+def test_d256_full_size_band_sampled():
+    """band8k_d256 (B=1 H=16 N=8192 d=256, band (2047, 0)), in the launch bench.py
+    times: sampled rows (band edges, tile edges, random) of sampled heads, and
+    every output finite and inside the range of V."""
+    import aware_attention_amd as aa
+    from tests.test_gpu_band import assert_l_band
+    torch = torch_or_skip()
+    w = W.WORKLOADS["band8k_d256"]
+    say(f"full-size band8k_d256 B={w.B} N={w.N} H={w.H} d={w.d} window={w.window}")
+    q, k, v = W.make_dense(w.B, w.N, w.H, w.d, w.seed)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = aa.fa_fwd(qd, kd, vd, softmax_scale=w.scale, window=w.window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 100)
+    fixed = {0, 1, 63, 64, 127, 128, 2046, 2047, 2048, 2049, w.N // 2, w.N - 2, w.N - 1}
+    for h in sorted({0, w.H - 1} | {int(rng.integers(w.H)) for _ in range(2)}):
+        rows = sorted(fixed | set(rng.integers(0, w.N, size=40).tolist()))
+        oref, lref = attention_dense(to_f64(q[:, :, h:h + 1]), to_f64(k[:, :, h:h + 1]),
+                                     to_f64(v[:, :, h:h + 1]), w.scale, rows=rows,
+                                     window=w.window)
+        assert_o_close(o_to_f64(o[0, rows, h]), oref[0, :, 0], f"band8k_d256 h={h}")
+        assert_l_band(lse[0, h, rows].cpu().numpy().astype(np.float64), lref[0, 0],
+                      f"band8k_d256 h={h}")
+    vmin = vd.float().amin(dim=1, keepdim=True)
+    vmax = vd.float().amax(dim=1, keepdim=True)
+    of = o.float()
+    slack = 1e-2 * (vmax - vmin) + 1e-3
+    assert torch.isfinite(of).all() and torch.isfinite(lse).all()
+    assert bool(((of >= vmin - slack) & (of <= vmax + slack)).all())

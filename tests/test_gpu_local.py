@@ -111,3 +111,25 @@ def test_local_deterministic():
     o2, l2 = aa.fa_fwd_local(q, k, v, 8, 40, (2, 2))
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_local_full_size_detlocal():
+    """detlocal (B=16 H=4, 8 anchors + 40 x 40 map, 5 x 5 window, d=32) in the
+    launch bench.py times, every output of 16 (batch, head) pairs against the
+    oracle and the rest finite."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    w = W.WORKLOADS["detlocal"]
+    G, Wd, wr, wc = w.local
+    say(f"full-size detlocal B={w.B} N={w.N} H={w.H} d={w.d} local={w.local}")
+    q, k, v = W.make_dense(w.B, w.N, w.H, w.d, w.seed)
+    o, lse = aa.fa_fwd_local(to_dev(q), to_dev(k), to_dev(v), G, Wd, (wr, wc),
+                             softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    batches = [0, 5, 10, 15]
+    oref, lref = attention_local_dense(to_f64(q), to_f64(k), to_f64(v), w.scale, G, Wd, wr, wc,
+                                       batches=batches)
+    assert_o_close(og[batches], oref, "detlocal O")
+    assert float(np.max(np.abs(lg[batches] - lref))) <= L_ATOL, "detlocal L"
+    assert np.isfinite(og).all() and np.isfinite(lg).all()

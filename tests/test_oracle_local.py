@@ -75,3 +75,44 @@ def test_local_mutant_is_caught(mutation):
         except Exception:  # noqa: BLE001 - any failure counts as caught
             failed.append(pin.__name__)
     assert failed, f"local mutation {mutation!r} passed every local pin"
+
+
+@pytest.mark.parametrize("G,Wd,wr,wc,causal", [(2, 3, 1, 0, False), (0, 4, 0, 1, True),
+                                               (3, 2, 1, 1, True), (1, 5, 0, 0, False)])
+def test_local_backward_finite_differences(G, Wd, wr, wc, causal):
+    """Gradients against central differences of the (pinned) local forward."""
+    from oracle.local import attention_local_backward
+    rng = np.random.default_rng(91 + G + 7 * Wd)
+    N = 9
+    q, k, v, do = (rng.standard_normal((N, 3)) for _ in range(4))
+
+    def loss(q_, k_, v_):
+        O, _ = attention_local(q_, k_, v_, 0.7, G, Wd, wr, wc, causal)
+        return float(np.sum(O * do))
+    dq, dk, dv, delta = attention_local_backward(q, k, v, do, 0.7, G, Wd, wr, wc, causal)
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            up = loss(q, k, v)
+            x[idx] = x0 - h
+            dn = loss(q, k, v)
+            x[idx] = x0
+            fd[idx] = (up - dn) / (2 * h)
+        np.testing.assert_allclose(g, fd, atol=1e-7)
+    O, _ = attention_local(q, k, v, 0.7, G, Wd, wr, wc, causal)
+    np.testing.assert_allclose(delta, np.sum(do * O, axis=1), atol=1e-12)
+
+
+def test_local_backward_one_wide_map_is_the_band_backward():
+    from oracle import attention_backward
+    from oracle.local import attention_local_backward
+    rng = np.random.default_rng(95)
+    q, k, v, do = (rng.standard_normal((12, 4)) for _ in range(4))
+    for causal in (False, True):
+        got = attention_local_backward(q, k, v, do, 0.5, 0, 1, 2, 7, causal)
+        ref = attention_backward(q, k, v, do, 0.5, window=(2, 0 if causal else 2))
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a, b, atol=1e-12)
