@@ -43,7 +43,7 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
                    FA_ERR_UNSUPPORTED, FA_OK, FaError, check, decode_workspace_bytes, load,
                    raw_fa_bwd, raw_fa_bwd_band, raw_fa_bwd_padded, raw_fa_bwd_varlen,
-                   raw_fa_bwd_varlen_band, raw_fa_decode, raw_fa_fwd_local,
+                   raw_fa_bwd_local, raw_fa_bwd_varlen_band, raw_fa_decode, raw_fa_fwd_local,
                    raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
                    raw_fa_fwd_varlen,
                    raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
@@ -224,9 +224,10 @@ def _check_contiguous(ts, names, dtype):
 
 
 def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None,
-           delta=None, window=None, key_padding_mask=None):
-    """Backward over an equal-length batch; returns (dq, dk, dv, delta). window and
-    key_padding_mask are those of the forward call (fa_bwd_band, fa_bwd_padded)."""
+           delta=None, window=None, key_padding_mask=None, local=None):
+    """Backward over an equal-length batch; returns (dq, dk, dv, delta). window,
+    key_padding_mask and local = (n_global, map_w, win_rows, win_cols) are those of
+    the forward call (fa_bwd_band, fa_bwd_padded, fa_bwd_local)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check_tensor(t, n, 4)
@@ -252,7 +253,14 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=
     dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if key_padding_mask is not None:
+        if local is not None:
+            if window is not None or key_padding_mask is not None or Nk != Nq:
+                raise ValueError("local: self-attention only, without a window or padding mask")
+            clamp = lambda x: max(min(int(x), 2**31 - 1), -1)  # noqa: E731
+            G, mw, wr, wc = (clamp(x) for x in local)
+            check(raw_fa_bwd_local(*ptrs, B, Nq, H, d, dt, scale, int(bool(causal)), G, mw, wr,
+                                   wc, stream))
+        elif key_padding_mask is not None:
             m = key_padding_mask
             if window is not None or Nk != Nq:
                 raise ValueError("key_padding_mask: self-attention only, and not with a window")
@@ -314,13 +322,20 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, softmax_scale, causal, window, key_padding_mask):
+        def forward(ctx, q, k, v, softmax_scale, causal, window, key_padding_mask, local):
             q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-            o, lse = fa_fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window=window,
-                            key_padding_mask=key_padding_mask)
+            if local is not None:
+                if window is not None or key_padding_mask is not None:
+                    raise ValueError("local excludes window and key_padding_mask")
+                G, mw, wr, wc = local
+                o, lse = fa_fwd_local(q, k, v, G, mw, (wr, wc), softmax_scale=softmax_scale,
+                                      causal=causal)
+            else:
+                o, lse = fa_fwd(q, k, v, softmax_scale=softmax_scale, causal=causal,
+                                window=window, key_padding_mask=key_padding_mask)
             ctx.save_for_backward(q, k, v, o, lse)
             ctx.softmax_scale, ctx.causal, ctx.window = softmax_scale, causal, window
-            ctx.key_padding_mask = key_padding_mask
+            ctx.key_padding_mask, ctx.local = key_padding_mask, local
             return o
 
         @staticmethod
@@ -328,8 +343,9 @@ def _autograd_function():
             q, k, v, o, lse = ctx.saved_tensors
             dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, dout.contiguous(),
                                    softmax_scale=ctx.softmax_scale, causal=ctx.causal,
-                                   window=ctx.window, key_padding_mask=ctx.key_padding_mask)
-            return dq, dk, dv, None, None, None, None
+                                   window=ctx.window, key_padding_mask=ctx.key_padding_mask,
+                                   local=ctx.local)
+            return dq, dk, dv, None, None, None, None, None
 
     return _Attention
 
@@ -337,14 +353,16 @@ def _autograd_function():
 _ATTENTION_FN = None
 
 
-def attention(q, k, v, softmax_scale=None, causal=False, window=None, key_padding_mask=None):
+def attention(q, k, v, softmax_scale=None, causal=False, window=None, key_padding_mask=None,
+              local=None):
     """o = softmax(scale q k^T) v over (B, N, H, d) tensors, differentiable: the
-    forward is fa_fwd and the backward fa_bwd (both HIP kernels), with the same
-    causal flag, band or key padding mask."""
+    forward is fa_fwd (fa_fwd_local with local = (n_global, map_w, win_rows,
+    win_cols)) and the backward fa_bwd (all HIP kernels), with the same causal
+    flag, band, key padding mask or local pattern."""
     global _ATTENTION_FN
     if _ATTENTION_FN is None:
         _ATTENTION_FN = _autograd_function()
-    return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal, window, key_padding_mask)
+    return _ATTENTION_FN.apply(q, k, v, softmax_scale, causal, window, key_padding_mask, local)
 
 
 def fa_fwd_local(q, k, v, n_global, map_w, window, softmax_scale=None, causal=False, out=None,

@@ -19,7 +19,7 @@ FA_DTYPE_F16 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
             "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_bwd_band",
-            "fa_bwd_varlen_band", "fa_bwd_padded", "fa_decode", "fa_fwd_local",
+            "fa_bwd_varlen_band", "fa_bwd_padded", "fa_decode", "fa_fwd_local", "fa_bwd_local",
             "fa_decode_workspace_bytes", "fa_status_string",
             "fa_last_error", "fa_abi_version")
 
@@ -70,6 +70,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_padded.restype = i32
     lib.fa_fwd_local.argtypes = [vp] * 5 + [i32] * 5 + [f32] + [i32] * 5 + [vp]
     lib.fa_fwd_local.restype = i32
+    lib.fa_bwd_local.argtypes = [vp] * 10 + [i32] * 5 + [f32] + [i32] * 5 + [vp]
+    lib.fa_bwd_local.restype = i32
     lib.fa_decode.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
     lib.fa_decode.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -177,6 +179,13 @@ def raw_fa_fwd_local(q, k, v, o, lse, B, N, H, d, dtype, scale, causal, n_global
     """Pointer-level call of fa_fwd_local; returns the status code."""
     return load().fa_fwd_local(q, k, v, o, lse, B, N, H, d, dtype, scale, causal, n_global,
                                map_w, win_rows, win_cols, stream)
+
+
+def raw_fa_bwd_local(q, k, v, o, dout, lse, dq, dk, dv, delta, B, N, H, d, dtype, scale, causal,
+                     n_global, map_w, win_rows, win_cols, stream) -> int:
+    """Pointer-level call of fa_bwd_local; returns the status code."""
+    return load().fa_bwd_local(q, k, v, o, dout, lse, dq, dk, dv, delta, B, N, H, d, dtype, scale,
+                               causal, n_global, map_w, win_rows, win_cols, stream)
 
 
 def decode_workspace_bytes(B, Nk, H, d) -> int:

@@ -1,8 +1,9 @@
-// C ABI of the backward pass (fa_bwd, fa_bwd_varlen, and their band and
-// padding-mask forms): argument checks and the three launches. The operation
-// is documented in include/fa.h.
+// C ABI of the backward pass (fa_bwd, fa_bwd_varlen, and their band,
+// padding-mask and local-window forms): argument checks and the three
+// launches. The operation is documented in include/fa.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -17,40 +18,44 @@ using fa_host::aligned16;
 using fa_host::check_device;
 using fa_host::fail;
 
-template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
+template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND, bool KPM, bool LOCAL>
 hipError_t launch_bwd_t(const fa::BwdParams& p, int64_t nrows, int N, uint32_t grid_k,
                         uint32_t grid_q, hipStream_t stream) {
   hipLaunchKernelGGL((fa::delta_kernel<D, F16>), dim3((uint32_t)((nrows + 255) / 256)), dim3(256),
                      0, stream, p.o, p.dout, p.delta, nrows, p.H, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM>), dim3(grid_k),
+  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>), dim3(grid_k),
                      dim3(fa::kBwdThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   fa::BwdParams pq = p;
   pq.n_tiles = (int32_t)(grid_q / (uint32_t)(p.H * p.nbatch));
-  hipLaunchKernelGGL((fa::dq_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM>), dim3(grid_q),
+  hipLaunchKernelGGL((fa::dq_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>), dim3(grid_q),
                      dim3(fa::kBwdThreads), 0, stream, pq);
   return hipGetLastError();
 }
 
-template <bool CAUSAL, bool VARLEN, bool F16, bool BAND, bool KPM>
+template <bool CAUSAL, bool VARLEN, bool F16, bool BAND, bool KPM, bool LOCAL = false>
 hipError_t launch_bwd_d(const fa::BwdParams& p, int d, int64_t nrows, int N, uint32_t grid_k,
                         uint32_t grid_q, hipStream_t stream) {
   switch (d) {
     case 32:
-      return launch_bwd_t<32, CAUSAL, VARLEN, F16, BAND, KPM>(p, nrows, N, grid_k, grid_q, stream);
+      return launch_bwd_t<32, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>(p, nrows, N, grid_k, grid_q,
+                                                                   stream);
     case 64:
-      return launch_bwd_t<64, CAUSAL, VARLEN, F16, BAND, KPM>(p, nrows, N, grid_k, grid_q, stream);
+      return launch_bwd_t<64, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>(p, nrows, N, grid_k, grid_q,
+                                                                   stream);
     default:
-      return launch_bwd_t<128, CAUSAL, VARLEN, F16, BAND, KPM>(p, nrows, N, grid_k, grid_q, stream);
+      return launch_bwd_t<128, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>(p, nrows, N, grid_k, grid_q,
+                                                                    stream);
   }
 }
 
-// Mask of a backward launch: none, causal, a band (dense or varlen), or a key
-// padding mask (dense), alone or with causal.
-enum class BwdMask { kNone, kCausal, kBand, kPad, kPadCausal };
+// Mask of a backward launch: none, causal, a band (dense or varlen), a key
+// padding mask (dense) or the local window + anchor pattern (dense), the last
+// two alone or with causal.
+enum class BwdMask { kNone, kCausal, kBand, kPad, kPadCausal, kLocal, kLocalCausal };
 
 template <bool VARLEN, bool F16>
 hipError_t launch_bwd_m(const fa::BwdParams& p, int d, BwdMask mask, int64_t nrows, int N,
@@ -66,6 +71,16 @@ hipError_t launch_bwd_m(const fa::BwdParams& p, int d, BwdMask mask, int64_t nro
         return mask == BwdMask::kPad
                    ? launch_bwd_d<false, false, F16, false, true>(p, d, nrows, N, grid_k, grid_q, stream)
                    : launch_bwd_d<true, false, F16, false, true>(p, d, nrows, N, grid_k, grid_q, stream);
+      }
+      return hipErrorInvalidValue;
+    case BwdMask::kLocal:
+    case BwdMask::kLocalCausal:
+      if constexpr (!VARLEN) {
+        return mask == BwdMask::kLocal
+                   ? launch_bwd_d<false, false, F16, false, false, true>(p, d, nrows, N, grid_k,
+                                                                         grid_q, stream)
+                   : launch_bwd_d<true, false, F16, false, false, true>(p, d, nrows, N, grid_k,
+                                                                        grid_q, stream);
       }
       return hipErrorInvalidValue;
     default:
@@ -111,11 +126,18 @@ bool all_aligned(const void* const* ptrs, int n) {
 
 constexpr float kLog2eHost = 1.44269504088896340736f;
 
+// Local window + anchors of fa_bwd_local (the forward's fa_fwd_local pattern).
+struct LocalPattern {
+  int32_t n_global, map_w, win_rows, win_cols;
+};
+constexpr int32_t kMaxLocalTokensBwd = 1 << 28;   // keeps the map arithmetic in int32
+
 fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
                     int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
                     float softmax_scale, int32_t causal, BwdMask mask, int32_t win_left,
-                    int32_t win_right, const uint8_t* kpm, void* stream) {
+                    int32_t win_right, const uint8_t* kpm, void* stream,
+                    const LocalPattern* loc = nullptr) {
   const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
   for (const void* x : ptrs)
     if (!x) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -125,6 +147,8 @@ fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, 
   if (causal && Nq != Nk) return fail(FA_ERR_INVALID_ARGUMENT, "causal attention needs Nq == Nk");
   if (mask == BwdMask::kBand && (Nq > kMaxBandLenBwd || Nk > kMaxBandLenBwd))
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports Nq, Nk <= 2^29");
+  if (loc && Nq > kMaxLocalTokensBwd)
+    return fail(FA_ERR_UNSUPPORTED, "local attention supports N <= 2^28");
   if (!all_aligned(ptrs, 10)) return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const int64_t units = (int64_t)H * B;
   const int64_t grid_k = (Nk + fa::kBwdRows - 1) / fa::kBwdRows * units;
@@ -164,6 +188,16 @@ fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.band_off = Nk - Nq;
   p.kpm = kpm;
   p.kpm_batch_stride = Nk;
+  if (loc) {   // sizes beyond the map's extent change nothing: clamp them (as the forward)
+    const int32_t G = std::min(loc->n_global, Nq);
+    const int32_t rest = Nq - G;
+    const int32_t W = std::min(loc->map_w, std::max(1, rest));
+    const int32_t rows = rest > 0 ? (rest + W - 1) / W : 0;
+    p.n_global = G;
+    p.map_w = W;
+    p.loc_rows = std::min(loc->win_rows, rows);
+    p.loc_cols = std::min(loc->win_cols, W);
+  }
   const hipError_t e = launch_bwd<false>(p, d, dtype, mask, nrows, Nq, (uint32_t)grid_k,
                                          (uint32_t)grid_q, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
@@ -299,6 +333,22 @@ fa_status fa_bwd_padded(const void* q, const void* k, const void* v, const void*
   return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, S, S, H, d, dtype, softmax_scale,
                    causal, causal ? BwdMask::kPadCausal : BwdMask::kPad, -1, -1, key_padding_mask,
                    stream);
+}
+
+fa_status fa_bwd_local(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       float* delta, int32_t B, int32_t N, int32_t H, int32_t d, int32_t dtype,
+                       float softmax_scale, int32_t causal, int32_t n_global, int32_t map_w,
+                       int32_t win_rows, int32_t win_cols, void* stream) {
+  fa_host::g_last_error.clear();
+  if (n_global < 0 || map_w < 1 || win_rows < 0 || win_cols < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "need n_global >= 0, map_w >= 1, win_rows >= 0, win_cols >= 0");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  const LocalPattern loc{n_global, map_w, win_rows, win_cols};
+  return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, N, N, H, d, dtype, softmax_scale,
+                   causal, causal ? BwdMask::kLocalCausal : BwdMask::kLocal, -1, -1, nullptr,
+                   stream, &loc);
 }
 
 }  // extern "C"

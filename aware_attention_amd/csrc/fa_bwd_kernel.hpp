@@ -64,6 +64,12 @@ struct BwdParams {
   // kpm[b * kpm_batch_stride + n] != 0.
   const uint8_t* kpm;
   int64_t kpm_batch_stride;
+  // Local window + global anchors (LOCAL instances, dense, Nq == Nk): tokens
+  // [0, n_global) are anchors, the rest a row-major map of map_w tokens per
+  // row; query i sees key j iff i or j is an anchor or their map positions
+  // differ by at most loc_rows rows and loc_cols columns (sizes clamped to
+  // the map's extent by the host).
+  int32_t n_global, map_w, loc_rows, loc_cols;
 };
 
 constexpr int kBwdWaves = 4;
@@ -157,6 +163,31 @@ __device__ __forceinline__ bf16x8 lds_tr8(const uint8_t* smem, int byte, int byt
   const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint8_t*)smem + byte_up));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Map position of token t in the local pattern (tokens [0, G) are anchors,
+// the rest a row-major map of W tokens per row): row and column, or the row
+// kKeyAnchor for an anchor and kKeyPast for a token at or past N. Two
+// positions are near iff their rows differ by at most wr and their columns by
+// at most wc; the sentinels are never near anything (|sentinel| >= 2^30 and
+// map rows, wr < 2^28).
+constexpr int kKeyAnchor = -(1 << 30);
+constexpr int kKeyPast = 1 << 30;
+__device__ __forceinline__ void map_pos(int t, int G, int W, int N, int& r, int& c) {
+  r = kKeyPast;
+  c = 0;
+  if (t < G) {
+    r = kKeyAnchor;
+  } else if (t < N) {
+    r = (t - G) / W;
+    c = (t - G) - r * W;
+  }
+}
+__device__ __forceinline__ bool map_near(int r1, int c1, int r2, int c2, int wr, int wc) {
+  return ((uint32_t)(r1 - r2 + wr) <= (uint32_t)(2 * wr)) &
+         ((uint32_t)(c1 - c2 + wc) <= (uint32_t)(2 * wc));
 }
 
 // A lane's 32 keys of a 64-key tile are the 4-key groups 8 g + 4 (l/32) + 0..3
@@ -265,17 +296,21 @@ __device__ __forceinline__ KpmSpan kpm_span(const uint8_t* row, int n, int* red,
   return {lo, hi, cnt == hi - lo + 1};
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
+template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false,
+          bool LOCAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
+  static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = kBwdTile * RBP;
-  // [Q 0][dO 0][Q 1][dO 1][L 0][D 0][L 1][D 1]: buffer b holds query tile
-  // qt0 + 2 m + b; L (times log2 e) and D per query of the tile.
+  // [Q 0][dO 0][Q 1][dO 1][L 0][D 0][L 1][D 1]: buffer b holds the visited
+  // query tiles b, b + 2, ...; L (times log2 e) and D per query of the tile.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB + 4 * kBwdTile * 4];
+  // Local pattern: map row and column of each query of the tile in buffer b.
+  __shared__ __attribute__((aligned(16))) int qmap[LOCAL ? 4 * kBwdTile : 4];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -334,6 +369,38 @@ void dkdv_kernel(BwdParams p) {
     }
   }
   const bool wave_has = kw0 < u.Nk && (!KPM || (kw0 <= span.hi && kw0 + 31 >= span.lo));
+  // Visited query tiles: [0, A) then [W0, W1) (without the local pattern A = 0,
+  // [W0, W1) = [qt0, n_qt)). Local pattern: an anchor key is seen by every
+  // query; a map key by the anchor queries (not when causal: they precede it)
+  // and by the map queries within loc_rows rows. A wave skips a tile in which
+  // none of its keys is seen.
+  int A = 0, W0 = qt0, W1 = n_qt;
+  const int G = p.n_global, MW = p.map_w, WR = p.loc_rows, WC = p.loc_cols;
+  int kmr = 0, kmc = 0;                 // this lane's key on the map
+  bool wave_anchor = false;             // the wave holds an anchor key
+  int wqlo = 0, wqhi = u.Nq - 1;        // queries that see the wave's map keys
+  if constexpr (LOCAL) {
+    map_pos(krow, G, MW, u.Nk, kmr, kmc);
+    const int k1 = min(u.Nk, k0 + kBwdRows);
+    if (k0 >= G) {
+      const int r_lo = (k0 - G) / MW, r_hi = (k1 - 1 - G) / MW;
+      int qlo = G + max(0, r_lo - WR) * MW;
+      const int qhi = min(u.Nq, G + (r_hi + WR + 1) * MW) - 1;
+      if (CAUSAL) qlo = max(qlo, k0);
+      A = CAUSAL ? 0 : min((G + kBwdTile - 1) / kBwdTile, n_qt);
+      W0 = max(A, qlo / kBwdTile);
+      W1 = max(W0, qhi / kBwdTile + 1);
+    }
+    wave_anchor = kw0 < G;
+    if (wave_has && !wave_anchor) {
+      const int kw1 = min(u.Nk, kw0 + 32) - 1;
+      const int r_lo = (kw0 - G) / MW, r_hi = (kw1 - G) / MW;
+      wqlo = G + max(0, r_lo - WR) * MW;
+      wqhi = min(u.Nq, G + (r_hi + WR + 1) * MW) - 1;
+    }
+  }
+  const int n_iter = A + max(0, W1 - W0);
+  auto tile_of = [&](int it) { return it < A ? it : W0 + (it - A); };
   // Copies of query tile qt into buffer b, and its L, D values into registers
   // (threads 0..63, one query each; padding queries get L = +inf, D = 0).
   auto issue = [&](int qt, int b) __attribute__((always_inline)) {
@@ -347,35 +414,47 @@ void dkdv_kernel(BwdParams p) {
     lv = qv ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
     dv_ = qi < u.Nq ? p.delta[u.l_off + qi] : 0.f;
   };
-  auto store_ld = [&](int b, float lv, float dv_) __attribute__((always_inline)) {
+  auto store_ld = [&](int b, int qt, float lv, float dv_) __attribute__((always_inline)) {
     float* ld = reinterpret_cast<float*>(smem + 4 * TB) + b * 2 * kBwdTile;
     ld[tid] = lv;
     ld[kBwdTile + tid] = dv_;
+    if constexpr (LOCAL) {
+      int r, c;
+      map_pos(qt * kBwdTile + tid, G, MW, u.Nq, r, c);
+      qmap[b * 2 * kBwdTile + tid] = r;
+      qmap[b * 2 * kBwdTile + kBwdTile + tid] = c;
+    }
   };
-  if (qt0 < n_qt) {
-    issue(qt0, 0);
+  if (n_iter > 0) {
+    issue(tile_of(0), 0);
     if (tid < kBwdTile) {
       float lv, dv_;
-      load_ld(qt0, lv, dv_);
-      store_ld(0, lv, dv_);
+      load_ld(tile_of(0), lv, dv_);
+      store_ld(0, tile_of(0), lv, dv_);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int qt = qt0; qt < n_qt; ++qt) {
+  for (int it = 0; it < n_iter; ++it) {
+    const int qt = tile_of(it);
     const int qb0 = qt * kBwdTile;
-    const int buf = (qt - qt0) & 1;
-    const bool more = qt + 1 < n_qt;
+    const int buf = it & 1;
+    const bool more = it + 1 < n_iter;
+    const int qt_next = more ? tile_of(it + 1) : 0;
     float nl = 0.f, nd = 0.f;
     if (more) {   // the other buffer was last read before the previous barrier
-      issue(qt + 1, buf ^ 1);
-      if (tid < kBwdTile) load_ld(qt + 1, nl, nd);
+      issue(qt_next, buf ^ 1);
+      if (tid < kBwdTile) load_ld(qt_next, nl, nd);
     }
     const uint8_t* q_lds = smem + (2 * buf) * TB;
     const uint8_t* do_lds = smem + (2 * buf + 1) * TB;
     const float* l_lds = reinterpret_cast<const float*>(smem + 4 * TB) + buf * 2 * kBwdTile;
     const float* d_lds = l_lds + kBwdTile;
-    if (wave_has && !(CAUSAL && qb0 + kBwdTile - 1 < kw0)) {
+    bool useful = wave_has && !(CAUSAL && qb0 + kBwdTile - 1 < kw0);
+    if constexpr (LOCAL)
+      useful = useful && (wave_anchor || (!CAUSAL && qb0 < G) ||
+                          (qb0 + kBwdTile - 1 >= wqlo && qb0 <= wqhi));
+    if (useful) {
 
     // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys.
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -401,6 +480,11 @@ void dkdv_kernel(BwdParams p) {
           const float4 L4 = *reinterpret_cast<const float4*>(l_lds + q4);
           const float4 D4 = *reinterpret_cast<const float4*>(d_lds + q4);
           const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+          i32x4 qmr = {0, 0, 0, 0}, qmc = {0, 0, 0, 0};
+          if constexpr (LOCAL) {
+            qmr = *reinterpret_cast<const i32x4*>(&qmap[buf * 2 * kBwdTile + q4]);
+            qmc = *reinterpret_cast<const i32x4*>(&qmap[buf * 2 * kBwdTile + kBwdTile + q4]);
+          }
           float pv[4], dsv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -408,6 +492,9 @@ void dkdv_kernel(BwdParams p) {
             const int qi = qb0 + q4 + e;
             bool ok = (!CAUSAL || krow <= qi) && k_valid;
             if constexpr (BAND) ok = ok && krow >= qi + band_lo && krow <= qi + band_hi;
+            if constexpr (LOCAL)
+              ok = ok & (map_near(qmr[e], qmc[e], kmr, kmc, WR, WC) | (qmr[e] == kKeyAnchor) |
+                         (kmr == kKeyAnchor));
             const float pe = ok ? __builtin_amdgcn_exp2f(s[qb][r] * p.scale_log2 - Lv[e]) : 0.f;
             pv[e] = pe;
             dsv[e] = pe * (dp[qb][r] - Dv[e]);
@@ -435,7 +522,7 @@ void dkdv_kernel(BwdParams p) {
       }
     }
     }
-    if (more && tid < kBwdTile) store_ld(buf ^ 1, nl, nd);
+    if (more && tid < kBwdTile) store_ld(buf ^ 1, qt_next, nl, nd);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }
@@ -445,16 +532,20 @@ void dkdv_kernel(BwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false>
+template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false,
+          bool LOCAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void dq_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
+  static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RBP = 2 * D + 16;
   constexpr int TB = kBwdTile * RBP;
-  // [K 0][V 0][K 1][V 1]: buffer b holds key tile 2 m + b.
+  // [K 0][V 0][K 1][V 1]: buffer b holds the visited key tiles b, b + 2, ...
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];
+  // Local pattern: map row and column of each key of the tile in buffer b.
+  __shared__ __attribute__((aligned(16))) int kmap[LOCAL ? 4 * kBwdTile : 4];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -518,21 +609,63 @@ void dq_kernel(BwdParams p) {
   }
   const bool wave_has = qw0 < u.Nq && (!KPM || (qw0 <= span.hi && qw0 + 31 >= span.lo));
   const int wave_last_kt = CAUSAL ? (qw0 + 31) / kBwdTile : n_kt - 1;
+  // Visited key tiles: [0, A) then [W0, W1) (without the local pattern A = 0,
+  // [W0, W1) = [kt_begin, kt_stop)). Local pattern: an anchor query sees every
+  // key; a map query sees the anchor keys and the map keys within loc_rows
+  // rows. A wave skips a tile in which none of its queries sees a key.
+  int A = 0, W0 = kt_begin, W1 = kt_stop;
+  const int G = p.n_global, MW = p.map_w, WR = p.loc_rows, WC = p.loc_cols;
+  int qmr = 0, qmc = 0;                 // this lane's query on the map
+  bool wave_anchor = false;             // the wave holds an anchor query
+  int wklo = 0, wkhi = u.Nk - 1;        // keys the wave's map queries see on the map
+  if constexpr (LOCAL) {
+    map_pos(qrow, G, MW, u.Nq, qmr, qmc);
+    if (q0 >= G) {
+      const int q1 = min(u.Nq, q0 + kBwdRows);
+      const int r_lo = (q0 - G) / MW, r_hi = (q1 - 1 - G) / MW;
+      const int klo = G + max(0, r_lo - WR) * MW;
+      const int khi = min(kend, G + (r_hi + WR + 1) * MW) - 1;
+      A = min((G + kBwdTile - 1) / kBwdTile, n_kt);
+      W0 = max(A, klo / kBwdTile);
+      W1 = max(W0, khi / kBwdTile + 1);
+    }
+    wave_anchor = qw0 < G;
+    if (wave_has && !wave_anchor) {
+      const int qw1 = min(u.Nq, qw0 + 32) - 1;
+      const int r_lo = (qw0 - G) / MW, r_hi = (qw1 - G) / MW;
+      wklo = G + max(0, r_lo - WR) * MW;
+      wkhi = min(u.Nk, G + (r_hi + WR + 1) * MW) - 1;
+    }
+  }
+  const int n_iter = A + max(0, W1 - W0);
+  auto tile_of = [&](int it) { return it < A ? it : W0 + (it - A); };
   auto issue = [&](int kt, int b) __attribute__((always_inline)) {
     copy_tile_async<D>(smem_lds + (2 * b) * TB, p.k + u.k_off, rs, kt * kBwdTile, u.Nk, wave, lane);
     copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.v + u.k_off, rs, kt * kBwdTile, u.Nk, wave,
                        lane);
+    if constexpr (LOCAL) {
+      if (tid < kBwdTile) {
+        int r, c;
+        map_pos(kt * kBwdTile + tid, G, MW, u.Nk, r, c);
+        kmap[b * 2 * kBwdTile + tid] = r;
+        kmap[b * 2 * kBwdTile + kBwdTile + tid] = c;
+      }
+    }
   };
-  if (kt_begin < kt_stop) issue(kt_begin, 0);
+  if (n_iter > 0) issue(tile_of(0), 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = kt_begin; kt < kt_stop; ++kt) {
+  for (int it = 0; it < n_iter; ++it) {
+    const int kt = tile_of(it);
     const int kb0 = kt * kBwdTile;
-    const int buf = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_stop) issue(kt + 1, buf ^ 1);   // buffer last read before the previous barrier
+    const int buf = it & 1;
+    if (it + 1 < n_iter) issue(tile_of(it + 1), buf ^ 1);   // buffer last read before the previous barrier
     const uint8_t* k_lds = smem + (2 * buf) * TB;
     const uint8_t* v_lds = smem + (2 * buf + 1) * TB;
-    if (wave_has && kt <= wave_last_kt) {
+    bool useful = wave_has && kt <= wave_last_kt;
+    if constexpr (LOCAL)
+      useful = useful && (wave_anchor || kb0 < G || (kb0 + kBwdTile - 1 >= wklo && kb0 <= wkhi));
+    if (useful) {
     uint32_t kvalid = ~0u;   // padding mask: validity bits of this lane's 32 keys
     if constexpr (KPM) {
       const int key = kb0 + lane;
@@ -561,6 +694,13 @@ void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v2[2];
+          // Map positions of this pair's keys (key index 4 (r/4)-aligned group).
+          const int kk = 32 * kb + 8 * ((8 * t + 2 * i) >> 2) + 4 * hi;
+          i32x4 kmr = {0, 0, 0, 0}, kmc = {0, 0, 0, 0};
+          if constexpr (LOCAL) {
+            kmr = *reinterpret_cast<const i32x4*>(&kmap[buf * 2 * kBwdTile + kk]);
+            kmc = *reinterpret_cast<const i32x4*>(&kmap[buf * 2 * kBwdTile + kBwdTile + kk]);
+          }
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * t + 2 * i + e;
@@ -568,6 +708,11 @@ void dq_kernel(BwdParams p) {
             bool ok = key < u.Nk && (!CAUSAL || key <= qrow);
             if constexpr (BAND) ok = ok && key >= qrow + band_lo && key <= qrow + band_hi;
             if constexpr (KPM) ok = ok && ((kvalid >> (16 * kb + r)) & 1);
+            if constexpr (LOCAL) {
+              const int j = r & 3;   // position of the key in its group of 4
+              ok = ok & (map_near(qmr, qmc, kmr[j], kmc[j], WR, WC) | (qmr == kKeyAnchor) |
+                         (kmr[j] == kKeyAnchor));
+            }
             const float pe = ok ? __builtin_amdgcn_exp2f(s[kb][r] * p.scale_log2 - Lq) : 0.f;
             v2[e] = pe * (dp[kb][r] - Dq);
           }

@@ -51,8 +51,6 @@ struct LocalParams {
   float scale_log2;           // softmax scale * log2(e)
 };
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kLocalRows = kBwdRows;            // queries per workgroup
 template <int D> constexpr int kLocalRing = D <= 64 ? 4 : 2;   // LDS tile slots
 
@@ -81,8 +79,6 @@ __device__ __forceinline__ void wait_tile(int newer) {
   }
   wait_vmcnt<0>();
 }
-constexpr int kKeyAnchor = -(1 << 30);          // map row stored for an anchor key
-constexpr int kKeyPast = 1 << 30;               // map row stored for a key past the end
 
 template <int D, bool CAUSAL, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
@@ -179,14 +175,8 @@ void fwd_local_kernel(LocalParams p) {
     copy_tile_async<D>(smem_lds + (2 * b) * TB, p.k + base, rs, kt * BC, N, wave, lane);
     copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.v + base, rs, kt * BC, N, wave, lane);
     if (!anchor_wg && tid < BC) {
-      const int j = kt * BC + tid;
-      int r = kKeyPast, c = 0;
-      if (j < G) {
-        r = kKeyAnchor;
-      } else if (j < N) {
-        r = (j - G) / W;
-        c = (j - G) - r * W;
-      }
+      int r, c;
+      map_pos(kt * BC + tid, G, W, N, r, c);
       kmrow[b][tid] = r;
       kmcol[b][tid] = c;
     }
@@ -250,9 +240,7 @@ void fwd_local_kernel(LocalParams p) {
               const int r = 4 * g + e;
               // Bitwise, not short-circuit, operators: one select per score
               // instead of divergent branches.
-              const bool near = ((uint32_t)(kr[e] - ir + WR) <= (uint32_t)(2 * WR)) &
-                                ((uint32_t)(kc[e] - ic + WC) <= (uint32_t)(2 * WC));
-              bool vis = near | (kr[e] == kKeyAnchor);
+              bool vis = map_near(kr[e], kc[e], ir, ic, WR, WC) | (kr[e] == kKeyAnchor);
               if (CAUSAL) vis = vis & (k0 + kk + e <= qrow);
               s[kb][r] = vis ? s[kb][r] * s2 : kNegInf;
               mt = fmaxf(mt, s[kb][r]);

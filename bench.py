@@ -139,6 +139,11 @@ def cpu_baseline_bwd(wl: dict, budget_s: float = 12.0):
                 attention_backward(f64(wl["q"])[:n], f64(wl["k"])[:n], f64(wl["v"])[:n],
                                    f64(do)[:n], spec.scale, spec.causal)
                 flops += 2.5 * 4.0 * n * n * spec.d / (2 if spec.causal else 1)
+            elif spec.local is not None:   # anchors + local window on the token map
+                from oracle import attention_local_backward
+                attention_local_backward(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), f64(do),
+                                         spec.scale, *spec.local, spec.causal)
+                flops += per_head
             else:
                 attention_backward(f64(wl["q"]), f64(wl["k"]), f64(wl["v"]), f64(do), spec.scale,
                                    spec.causal, window=spec.window)
@@ -258,9 +263,6 @@ def main():
                 aa.fa_fwd_local(q, k, v, G, map_w, (wr, wc), softmax_scale=spec.scale,
                                 causal=spec.causal, out=o, lse=lse)
 
-        if args.backward and spec.local is not None:
-            print("the local-window pattern has no backward", file=sys.stderr)
-            sys.exit(2)
         if args.backward:
             step()
             do = to_dev(W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0])
@@ -271,7 +273,7 @@ def main():
             def step():  # noqa: F811 - the timed step is the backward
                 aa.fa_bwd(q, k, v, o, lse, do, softmax_scale=spec.scale, causal=spec.causal,
                           dq=dq, dk=dk, dv=dv, delta=delta, window=spec.window,
-                          key_padding_mask=kpm)
+                          key_padding_mask=kpm, local=spec.local)
     else:
         if args.backward:
             print("--backward is measured on equal-length workloads", file=sys.stderr)

@@ -345,6 +345,19 @@ const char* fa_last_error(void);
 /* Version of this ABI (incremented on incompatible change). */
 int32_t fa_abi_version(void);
 
+/*
+ * Backward of fa_fwd_local (local window on a token map plus global
+ * anchors): the arguments of fa_bwd for self-attention (N queries and keys)
+ * with the pattern arguments of fa_fwd_local. Pairs outside the pattern carry
+ * no gradient. Errors: as fa_bwd; a negative pattern size or map_w < 1 is
+ * FA_ERR_INVALID_ARGUMENT; N above 2^28 is FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_bwd_local(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       float* delta, int32_t B, int32_t N, int32_t H, int32_t d, int32_t dtype,
+                       float softmax_scale, int32_t causal, int32_t n_global, int32_t map_w,
+                       int32_t win_rows, int32_t win_cols, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

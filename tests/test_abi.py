@@ -470,3 +470,20 @@ def test_local_argument_checks():
         assert lib.raw_fa_fwd_local(*args, 2, 1608, 4, 32, bf, 0.1, 1, 8, 40, 2, 2, None) == HIP
         assert lib.raw_fa_fwd_local(*args, 1, 100, 2, 256, lib.FA_DTYPE_F16, 0.0, 0, 1000, 1, 0,
                                     0, None) == HIP
+
+
+def test_bwd_local_argument_checks():
+    _lib_or_skip()
+    lib = _lib
+    args = [P] * 10
+    bf = lib.FA_DTYPE_BF16
+    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, -1, 10, 2, 2, None) == INV
+    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 0, 2, 2, None) == INV
+    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 10, -1, 2, None) == INV
+    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 2, 4, 10, 2, 2, None) == INV
+    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 256, bf, 0.1, 0, 4, 10, 2, 2, None) == UNS
+    assert lib.raw_fa_bwd_local(*args, 1, (1 << 28) + 1, 2, 64, bf, 0.1, 0, 4, 10, 2, 2,
+                                None) == UNS
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert lib.raw_fa_bwd_local(*args, 2, 408, 2, 64, bf, 0.1, 1, 8, 20, 2, 2, None) == HIP

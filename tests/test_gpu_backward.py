@@ -387,3 +387,87 @@ def test_autograd_with_band_and_padding_mask():
         torch.cuda.synchronize()
         for a, b_ in zip((qa.grad, ka.grad, va.grad), g[:3]):
             assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), str(kw.keys())
+
+
+# ---------------------------------------------------------------------------
+# Backward of the local window + global anchor pattern
+# ---------------------------------------------------------------------------
+
+from oracle import attention_local_backward_dense, attention_local_dense, local_visible  # noqa: E402
+
+
+def _local_terms(qf, kf, vf, dof, scale, G, Wd, wr, wc, causal, eps):
+    """D-rounding bounds (module docstring) with the local pattern's P."""
+    B, N, H, _ = qf.shape
+    vis = local_visible(N, G, Wd, wr, wc, causal)
+    tq, tk = np.zeros_like(qf), np.zeros_like(kf)
+    for b in range(B):
+        for h in range(H):
+            S = np.where(vis, scale * qf[b, :, h] @ kf[b, :, h].T, -np.inf)
+            e = np.exp(S - S.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            tq[b, :, h], tk[b, :, h], _ = d_rounding_terms(
+                qf[b, :, h], kf[b, :, h], vf[b, :, h], dof[b, :, h], scale, causal, eps, P=P)
+    return tq, tk
+
+
+def check_bwd_local(B, N, H, d, G, Wd, win, causal, seed):
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    wr, wc = win
+    say(f"bwd local B={B} N={N} H={H} d={d} G={G} map_w={Wd} win={win} causal={causal} "
+        f"seed={seed}")
+    q, k, v = W.make_dense(B, N, H, d, seed)
+    do = W.make_dense(B, N, H, d, seed + 1)[0]
+    scale = 1 / np.sqrt(d)
+    qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
+    oref, lref = attention_local_dense(qf, kf, vf, scale, G, Wd, wr, wc, causal)
+    dq, dk, dv, delta = aa.fa_bwd(to_dev(q), to_dev(k), to_dev(v), to_dev(_round(oref, "bf16")),
+                                  torch.from_numpy(lref.astype(np.float32)).cuda(), to_dev(do),
+                                  softmax_scale=scale, causal=causal, local=(G, Wd, wr, wc))
+    torch.cuda.synchronize()
+    gq, gk, gv, gd = attention_local_backward_dense(qf, kf, vf, dof, scale, G, Wd, wr, wc, causal)
+    tq, tk = _local_terms(qf, kf, vf, dof, scale, G, Wd, wr, wc, causal, EPS_O["bf16"])
+    what = f"local G={G} map_w={Wd} win={win} causal={causal} N={N} d={d}"
+    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
+    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
+    assert_grad_close(_np(dv), gv, "dv " + what)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_local_detector_map(d, causal):
+    # 8 anchors + a 20 x 20 map, 5 x 5 window.
+    check_bwd_local(2, 8 + 400, 2, d, 8, 20, (2, 2), causal, seed=14000 + d + causal)
+
+
+@pytest.mark.parametrize("G,Wd,win", [(0, 1, (3, 0)), (70, 13, (0, 0)), (3, 17, (3, 1)),
+                                      (0, 40, (1, 1)), (5, 33, (100, 100))])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_local_patterns(G, Wd, win, causal):
+    check_bwd_local(1, 333, 2, 64, G, Wd, win, causal, seed=14100 + G + Wd)
+
+
+@pytest.mark.parametrize("N", [1, 65, 300])
+def test_bwd_local_lengths(N):
+    check_bwd_local(2, N, 2, 128, min(3, N), 9, (1, 2), N % 2 == 1, seed=14200 + N)
+
+
+def test_autograd_with_local_pattern():
+    """The autograd wrapper with local= runs fa_fwd_local and fa_bwd_local
+    (bitwise equal to the direct calls)."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    say("autograd with the local pattern")
+    q, k, v = (to_dev(x) for x in W.make_dense(2, 408, 2, 64, seed=14300))
+    do = to_dev(W.make_dense(2, 408, 2, 64, seed=14301)[0])
+    loc = (8, 20, 2, 2)
+    o, lse = aa.fa_fwd_local(q, k, v, 8, 20, (2, 2))
+    g = aa.fa_bwd(q, k, v, o, lse, do, local=loc)
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = aa.attention(qa, ka, va, local=loc)
+    out.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach().view(torch.int16), o.view(torch.int16))
+    for a, b_ in zip((qa.grad, ka.grad, va.grad), g[:3]):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
