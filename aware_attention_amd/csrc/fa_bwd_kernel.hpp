@@ -403,21 +403,35 @@ void dkdv_kernel(BwdParams p) {
   auto tile_of = [&](int it) { return it < A ? it : W0 + (it - A); };
   // Copies of query tile qt into buffer b, and its L, D values into registers
   // (threads 0..63, one query each; padding queries get L = +inf, D = 0).
+  // The loads are unconditional (index clamped into the row) and their values
+  // are used only in store_ld, after the tile's compute: a wait for them any
+  // earlier would also wait for the tile copies issued before them.
   auto issue = [&](int qt, int b) __attribute__((always_inline)) {
     copy_tile_async<D>(smem_lds + (2 * b) * TB, p.q + u.q_off, rs, qt * kBwdTile, u.Nq, wave, lane);
     copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.dout + u.q_off, rs, qt * kBwdTile, u.Nq, wave,
                        lane);
   };
-  auto load_ld = [&](int qt, float& lv, float& dv_) __attribute__((always_inline)) {
-    const int qi = qt * kBwdTile + tid;
-    const bool qv = qi < u.Nq && (!KPM || kpm_row[qi] != 0);
-    lv = qv ? p.lse[u.l_off + qi] * kLog2eF : __builtin_inff();
-    dv_ = qi < u.Nq ? p.delta[u.l_off + qi] : 0.f;
+  struct Ld {
+    float l, d;
+    uint8_t valid;   // padding mask byte (KPM)
   };
-  auto store_ld = [&](int b, int qt, float lv, float dv_) __attribute__((always_inline)) {
+  auto load_ld = [&](int qt, Ld& x) __attribute__((always_inline)) {
+    const int qc = min(qt * kBwdTile + tid, u.Nq - 1);
+    x.l = p.lse[u.l_off + qc];
+    x.d = p.delta[u.l_off + qc];
+    x.valid = KPM ? kpm_row[qc] : 1;
+  };
+  auto store_ld = [&](int b, int qt, const Ld& x) __attribute__((always_inline)) {
+    const int qi = qt * kBwdTile + tid;
+    // The empty asm takes the loaded values here, so that the arithmetic on
+    // them (and the wait for the loads) is not hoisted up to the loads.
+    float lraw = x.l, draw = x.d;
+    uint32_t vraw = x.valid;
+    asm volatile("" : "+v"(lraw), "+v"(draw), "+v"(vraw));
+    const bool qv = qi < u.Nq && vraw != 0;
     float* ld = reinterpret_cast<float*>(smem + 4 * TB) + b * 2 * kBwdTile;
-    ld[tid] = lv;
-    ld[kBwdTile + tid] = dv_;
+    ld[tid] = qv ? lraw * kLog2eF : __builtin_inff();
+    ld[kBwdTile + tid] = qi < u.Nq ? draw : 0.f;
     if constexpr (LOCAL) {
       int r, c;
       map_pos(qt * kBwdTile + tid, G, MW, u.Nq, r, c);
@@ -428,9 +442,9 @@ void dkdv_kernel(BwdParams p) {
   if (n_iter > 0) {
     issue(tile_of(0), 0);
     if (tid < kBwdTile) {
-      float lv, dv_;
-      load_ld(tile_of(0), lv, dv_);
-      store_ld(0, tile_of(0), lv, dv_);
+      Ld x;
+      load_ld(tile_of(0), x);
+      store_ld(0, tile_of(0), x);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -441,10 +455,10 @@ void dkdv_kernel(BwdParams p) {
     const int buf = it & 1;
     const bool more = it + 1 < n_iter;
     const int qt_next = more ? tile_of(it + 1) : 0;
-    float nl = 0.f, nd = 0.f;
+    Ld nx{0.f, 0.f, 0};
     if (more) {   // the other buffer was last read before the previous barrier
       issue(qt_next, buf ^ 1);
-      if (tid < kBwdTile) load_ld(qt_next, nl, nd);
+      if (tid < kBwdTile) load_ld(qt_next, nx);
     }
     const uint8_t* q_lds = smem + (2 * buf) * TB;
     const uint8_t* do_lds = smem + (2 * buf + 1) * TB;
@@ -522,7 +536,7 @@ void dkdv_kernel(BwdParams p) {
       }
     }
     }
-    if (more && tid < kBwdTile) store_ld(buf ^ 1, qt_next, nl, nd);
+    if (more && tid < kBwdTile) store_ld(buf ^ 1, qt_next, nx);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }
