@@ -471,3 +471,62 @@ def test_autograd_with_local_pattern():
     assert torch.equal(out.detach().view(torch.int16), o.view(torch.int16))
     for a, b_ in zip((qa.grad, ka.grad, va.grad), g[:3]):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Full-size backward of every timed workload, in the launch bench.py times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["prefill8k", "vit", "det1600", "band8k", "vitpad", "detlocal"])
+def test_bwd_full_size_workloads(name):
+    """Whole (batch, head) pairs against the oracle's gradients (one pair at
+    N = 8192, two elsewhere), and at every head the key-shift invariant (the
+    dK columns sum to zero relative to their scale) and finite gradients."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    w = W.WORKLOADS[name]
+    wl = W.make_workload(name)
+    say(f"bwd full-size {name} B={w.B} N={w.N} H={w.H} d={w.d}")
+    q, k, v = wl["q"], wl["k"], wl["v"]
+    do = W.make_dense(w.B, w.N, w.H, w.d, w.seed + 1)[0]
+    qd, kd, vd, dod = (to_dev(x) for x in (q, k, v, do))
+    mask = wl.get("mask")
+    kpm = torch.from_numpy(mask).cuda() if mask is not None else None
+    if w.local is not None:
+        G, mw, wr, wc = w.local
+        o, lse = aa.fa_fwd_local(qd, kd, vd, G, mw, (wr, wc), softmax_scale=w.scale,
+                                 causal=w.causal)
+    else:
+        o, lse = aa.fa_fwd(qd, kd, vd, softmax_scale=w.scale, causal=w.causal, window=w.window,
+                           key_padding_mask=kpm)
+    dq, dk, dv, _ = aa.fa_bwd(qd, kd, vd, o, lse, dod, softmax_scale=w.scale, causal=w.causal,
+                              window=w.window, key_padding_mask=kpm, local=w.local)
+    torch.cuda.synchronize()
+    pairs = [(0, w.H // 2)] if w.N > 4096 else [(0, 0), (w.B - 1, w.H - 1)]
+    for b, h in pairs:
+        sl = lambda x: to_f64(x[b:b + 1, :, h:h + 1])  # noqa: E731
+        qf, kf, vf, dof = sl(q), sl(k), sl(v), sl(do)
+        if w.local is not None:
+            gq, gk, gv, _ = attention_local_backward_dense(qf, kf, vf, dof, w.scale, *w.local,
+                                                           w.causal)
+            tq, tk = _local_terms(qf, kf, vf, dof, w.scale, *w.local, w.causal, EPS_O_HIP)
+        elif mask is not None:
+            gq, gk, gv, _ = attention_backward_padded(qf, kf, vf, dof, mask[b:b + 1], w.scale,
+                                                      w.causal)
+            tq, tk, _ = dense_terms(qf, kf, vf, dof, w.scale, w.causal, EPS_O_HIP,
+                                    mask=mask[b:b + 1])
+        else:
+            gq, gk, gv, _ = attention_backward_dense(qf, kf, vf, dof, w.scale, w.causal,
+                                                     window=w.window)
+            tq, tk, _ = dense_terms(qf, kf, vf, dof, w.scale, w.causal, EPS_O_HIP,
+                                    window=w.window)
+        what = f"{name} b={b} h={h}"
+        assert_grad_close(_np(dq[b:b + 1, :, h:h + 1]), gq, "dq " + what, extra=tq)
+        assert_grad_close(_np(dk[b:b + 1, :, h:h + 1]), gk, "dk " + what, extra=tk)
+        assert_grad_close(_np(dv[b:b + 1, :, h:h + 1]), gv, "dv " + what)
+    dkf = dk.double()
+    colsum = dkf.sum(dim=1).abs()                            # (B, H, d)
+    scale_ = dkf.abs().sum(dim=1)
+    assert torch.isfinite(dkf).all() and torch.isfinite(dq.double()).all()
+    assert torch.isfinite(dv.double()).all()
+    assert bool((colsum <= 2e-2 * scale_ + 1e-3).all()), float((colsum / (scale_ + 1e-30)).max())
