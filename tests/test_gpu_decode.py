@@ -80,3 +80,28 @@ def test_decode_matches_forward_and_is_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     assert_o_close(o_to_f64(o1), o_to_f64(of), "decode vs forward")
     assert float((l1 - lf[:, :, 0]).abs().max()) <= L_ATOL
+
+
+@pytest.mark.parametrize("name", ["decode8k", "decode32k"])
+def test_decode_full_size_workloads(name):
+    """decode8k / decode32k in the launch bench.py times (caller workspace,
+    preallocated outputs): every (batch, head) against the oracle."""
+    import aware_attention_amd as aa
+    torch = torch_or_skip()
+    w = W.WORKLOADS[name]
+    say(f"decode full-size {name} B={w.B} Nk={w.Nk} H={w.H} d={w.d}")
+    wl = W.make_workload(name)
+    q, k, v = (to_dev(x) for x in (wl["q"], wl["k"], wl["v"]))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(aa._lib.decode_workspace_bytes(w.B, w.Nk, w.H, w.d), dtype=torch.uint8,
+                     device="cuda")
+    aa.fa_decode(q, k, v, softmax_scale=w.scale, out=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    qf, kf, vf = to_f64(wl["q"]), to_f64(wl["k"]), to_f64(wl["v"])
+    for b in range(w.B):
+        for h in range(w.H):
+            oref, lref = attention(qf[b, :, h], kf[b, :, h], vf[b, :, h], w.scale)
+            assert_o_close(og[b, 0, h][None], oref, f"{name} O b={b} h={h}")
+            assert abs(lg[b, h] - lref[0]) <= L_ATOL, f"{name} L b={b} h={h}"
