@@ -152,12 +152,23 @@ void fwd256_kernel(FwdParams p) {
         kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(kv), hi);
       }
       // S^T = K Q^T: 64 keys x the wave's 32 queries, keys in accumulator rows.
+      // With one wave per SIMD nothing else hides the LDS latency: the K
+      // operands go through a ring of RA registers, each read issued RA
+      // products ahead of its use (sched_barrier keeps the reads and products
+      // in that order, letting only ALU work move across), instead of a read,
+      // a wait and a product in turn.
+      constexpr int RA = 4, NS = 2 * DS;   // steps st = (ds, kb) = (st / 2, st % 2)
+      auto k_off = [&](int st) { return (st & 1) * 32 * RBP + ln.row_rd + (st >> 1) * 32; };
       f32x16 s[2] = {f32x16{}, f32x16{}};
+      bf16x8 ka[RA];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
+      for (int st = 0; st < RA; ++st) ka[st] = lds16(k_lds, k_off(st));
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          s[kb] = mfma32<F16>(lds16(k_lds, kb * 32 * RBP + ln.row_rd + ds * 32), qr[ds], s[kb]);
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 a = ka[st % RA];
+        if (st + RA < NS) ka[st % RA] = lds16(k_lds, k_off(st + RA));
+        s[st & 1] = mfma32<F16>(a, qr[st >> 1], s[st & 1]);
+        __builtin_amdgcn_sched_barrier(0x7);   // only ALU work may cross
       }
       // Online softmax (base 2); masked keys (past the end, after the query
       // when causal, outside the band, padding) get -inf, only on the tiles
@@ -206,16 +217,24 @@ void fwd256_kernel(FwdParams p) {
           pb[kb][t] = __builtin_bit_cast(bf16x8, w);
         }
       }
-      // O^T += V^T P^T.
+      // O^T += V^T P^T, with the same read-ahead for the transposed V
+      // operands (steps st = (16-key group g = st / DB, column block st % DB)).
+      constexpr int NP = 4 * DB;
+      auto v_op = [&](int st) {
+        const int g = st / DB, b = st % DB;
+        const int r0 = (32 * (g >> 1) + 16 * (g & 1)) * RBP;
+        return lds_tr8(v_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]);
+      };
+      bf16x8 va[RA];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int st = 0; st < RA; ++st) va[st] = v_op(st);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r0 = (32 * kb + 16 * t) * RBP;
-#pragma unroll
-          for (int b = 0; b < DB; ++b)
-            o[b] = mfma32<F16>(lds_tr8(v_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), pb[kb][t], o[b]);
-        }
+      for (int st = 0; st < NP; ++st) {
+        const bf16x8 a = va[st % RA];
+        if (st + RA < NP) va[st % RA] = v_op(st + RA);
+        const int g = st / DB;
+        o[st % DB] = mfma32<F16>(a, pb[g >> 1][g & 1], o[st % DB]);
+        __builtin_amdgcn_sched_barrier(0x7);   // only ALU work may cross
       }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
