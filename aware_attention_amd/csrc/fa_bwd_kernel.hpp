@@ -76,6 +76,7 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;   // rows a workgroup owns
 constexpr int kBwdTile = 64;               // rows of a streamed LDS tile
+constexpr int kReadAhead = 4;              // LDS operand reads in flight ahead of the products (dQ)
 constexpr float kLog2eF = 1.44269504088896340736f;
 
 template <bool F16>
@@ -687,15 +688,29 @@ void dq_kernel(BwdParams p) {
       kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(kv), hi);
     }
 
-    // S^T = K Q^T and dP^T = V dO^T: this tile's 64 keys x the wave's 32 queries.
+    // S^T = K Q^T and dP^T = V dO^T: this tile's 64 keys x the wave's 32
+    // queries. With one wave per SIMD nothing else hides the LDS latency:
+    // operands go through a ring of kReadAhead registers, each read issued
+    // that many products ahead of its use (sched_barrier keeps reads and
+    // products in order and lets only ALU work cross). Step
+    // st = 4 ds + 2 kb + (0: S from K, 1: dP from V).
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    {
+      constexpr int NS = 4 * DS;
+      auto rd = [&](int st) {
+        return lds16((st & 1) ? v_lds : k_lds, ((st >> 1) & 1) * 32 * RBP + ln.row_rd + (st >> 2) * 32);
+      };
+      bf16x8 ra[kReadAhead];
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
+      for (int st = 0; st < kReadAhead; ++st) ra[st] = rd(st);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int off = kb * 32 * RBP + ln.row_rd + ds * 32;
-        s[kb] = mfma32<F16>(lds16(k_lds, off), qr[ds], s[kb]);
-        dp[kb] = mfma32<F16>(lds16(v_lds, off), dor[ds], dp[kb]);
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 a = ra[st % kReadAhead];
+        if (st + kReadAhead < NS) ra[st % kReadAhead] = rd(st + kReadAhead);
+        const int ds = st >> 2, kb = (st >> 1) & 1;
+        if (st & 1) dp[kb] = mfma32<F16>(a, dor[ds], dp[kb]);
+        else s[kb] = mfma32<F16>(a, qr[ds], s[kb]);
+        __builtin_amdgcn_sched_barrier(0x7);
       }
     }
     // dS^T = P^T (dP^T - D), packed as B operands.
@@ -735,15 +750,24 @@ void dq_kernel(BwdParams p) {
         dsb[kb][t] = __builtin_bit_cast(bf16x8, w);
       }
     }
-    // dQ^T += K^T dS^T.
+    // dQ^T += K^T dS^T, with the same read-ahead (step st = g DB + b, g = 2 kb + t).
+    {
+      constexpr int NP = 4 * DB;
+      auto rd = [&](int st) {
+        const int g = st / DB, b = st % DB;
+        const int r0 = (32 * (g >> 1) + 16 * (g & 1)) * RBP;
+        return lds_tr8(k_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]);
+      };
+      bf16x8 ra[kReadAhead];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int st = 0; st < kReadAhead; ++st) ra[st] = rd(st);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r0 = (32 * kb + 16 * t) * RBP;
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-          acc[b] = mfma32<F16>(lds_tr8(k_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), dsb[kb][t], acc[b]);
+      for (int st = 0; st < NP; ++st) {
+        const bf16x8 a = ra[st % kReadAhead];
+        if (st + kReadAhead < NP) ra[st % kReadAhead] = rd(st + kReadAhead);
+        const int g = st / DB;
+        acc[st % DB] = mfma32<F16>(a, dsb[g >> 1][g & 1], acc[st % DB]);
+        __builtin_amdgcn_sched_barrier(0x7);
       }
     }
     }
