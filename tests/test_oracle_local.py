@@ -116,3 +116,123 @@ def test_local_backward_one_wide_map_is_the_band_backward():
         ref = attention_backward(q, k, v, do, 0.5, window=(2, 0 if causal else 2))
         for a, b in zip(got, ref):
             np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The (B, N, H, d) wrappers that the GPU tests compare against: each (batch,
+# head) slice must be exactly the single-head result, in the documented
+# layouts (O (nb, N, nh, d), L (nb, nh, N); gradients in the input layouts,
+# delta (B, H, N)). B = 2 and H = 3 differ, so a swapped index or a
+# transposed output lands on the wrong slice and fails.
+# ---------------------------------------------------------------------------
+
+_PATTERN = (2, 4, 1, 1)   # n_global, map_w, win_rows, win_cols
+
+
+def _wrapper_inputs(seed):
+    rng = np.random.default_rng(seed)
+    B, N, H, d = 2, 14, 3, 4
+    return [rng.standard_normal((B, N, H, d)) for _ in range(4)]
+
+
+def _local_dense_wrapper_pin(wrapper):
+    q, k, v, _ = _wrapper_inputs(301)
+    for causal in (False, True):
+        O, L = wrapper(q, k, v, 0.6, *_PATTERN, causal)
+        assert O.shape == (2, 14, 3, 4) and L.shape == (2, 3, 14)
+        for b in range(2):
+            for h in range(3):
+                o, l = attention_local(q[b, :, h], k[b, :, h], v[b, :, h], 0.6, *_PATTERN, causal)
+                np.testing.assert_array_equal(O[b, :, h], o)
+                np.testing.assert_array_equal(L[b, h], l)
+        Os, Ls = wrapper(q, k, v, 0.6, *_PATTERN, causal, batches=[1], heads=[2, 0])
+        np.testing.assert_array_equal(Os[0, :, 0], O[1, :, 2])
+        np.testing.assert_array_equal(Os[0, :, 1], O[1, :, 0])
+        np.testing.assert_array_equal(Ls[0], L[1, [2, 0]])
+
+
+def _local_backward_dense_wrapper_pin(wrapper):
+    from oracle.local import attention_local_backward
+    q, k, v, do = _wrapper_inputs(302)
+    for causal in (False, True):
+        dq, dk, dv, delta = wrapper(q, k, v, do, 0.6, *_PATTERN, causal)
+        assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+        assert delta.shape == (2, 3, 14)
+        for b in range(2):
+            for h in range(3):
+                g = attention_local_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h],
+                                             0.6, *_PATTERN, causal)
+                for got, want in zip((dq[b, :, h], dk[b, :, h], dv[b, :, h], delta[b, h]), g):
+                    np.testing.assert_array_equal(got, want)
+
+
+def test_local_dense_wrapper_is_per_head():
+    from oracle.local import attention_local_dense
+    _local_dense_wrapper_pin(attention_local_dense)
+
+
+def test_local_backward_dense_wrapper_is_per_head():
+    from oracle.local import attention_local_backward_dense
+    _local_backward_dense_wrapper_pin(attention_local_backward_dense)
+
+
+def _mutant_local_dense(mutation):
+    def fn(q, k, v, scale, G, Wd, wr, wc, causal=False, batches=None, heads=None):
+        B, N, H, _ = q.shape
+        bs = list(range(B)) if batches is None else list(batches)
+        hs = list(range(H)) if heads is None else list(heads)
+        O = np.zeros((len(bs), N, len(hs), v.shape[3]))
+        L = np.zeros((len(bs), len(hs), N))
+        for bi, b in enumerate(bs):
+            for hi, h in enumerate(hs):
+                if mutation == "batch_head_swapped":   # reads slice (h mod B, b mod H)
+                    src = (h % B, b % H)
+                elif mutation == "head_off_by_one":
+                    src = (b, (h + 1) % H)
+                else:
+                    src = (b, h)
+                o, l = attention_local(q[src[0], :, src[1]], k[src[0], :, src[1]],
+                                       v[src[0], :, src[1]], scale, G, Wd, wr, wc, causal)
+                if mutation == "lse_rows_reversed":
+                    l = l[::-1]
+                O[bi, :, hi], L[bi, hi] = o, l
+        if mutation == "output_heads_reversed":
+            O = O[:, :, ::-1]
+        return O, L
+    return fn
+
+
+def _mutant_local_backward_dense(mutation):
+    from oracle.local import attention_local_backward
+
+    def fn(q, k, v, do, scale, G, Wd, wr, wc, causal=False):
+        B, N, H, _ = q.shape
+        dq, dk, dv = (np.zeros(x.shape) for x in (q, k, v))
+        delta = np.zeros((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                src_h = (h + 1) % H if mutation == "head_off_by_one" else h
+                g = attention_local_backward(q[b, :, src_h], k[b, :, src_h], v[b, :, src_h],
+                                             do[b, :, src_h], scale, G, Wd, wr, wc, causal)
+                if mutation == "dq_dk_swapped":
+                    g = (g[1], g[0], g[2], g[3])
+                dq[b, :, h], dk[b, :, h], dv[b, :, h], delta[b, h] = g
+        if mutation == "delta_transposed":
+            delta = np.ascontiguousarray(delta.transpose(1, 0, 2)).reshape(B, H, N)
+        return dq, dk, dv, delta
+    return fn
+
+
+@pytest.mark.parametrize("mutation", ["batch_head_swapped", "head_off_by_one",
+                                      "lse_rows_reversed", "output_heads_reversed"])
+def test_local_dense_wrapper_mutant_is_caught(mutation):
+    _local_dense_wrapper_pin(_mutant_local_dense("none"))
+    with pytest.raises(AssertionError):
+        _local_dense_wrapper_pin(_mutant_local_dense(mutation))
+
+
+@pytest.mark.parametrize("mutation", ["head_off_by_one", "dq_dk_swapped", "delta_transposed"])
+def test_local_backward_dense_wrapper_mutant_is_caught(mutation):
+    _local_backward_dense_wrapper_pin(_mutant_local_backward_dense("none"))
+    with pytest.raises(AssertionError):
+        _local_backward_dense_wrapper_pin(_mutant_local_backward_dense(mutation))
