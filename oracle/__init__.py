@@ -9,8 +9,9 @@ product path.
 Contents:
   attention.py  the plain definition of exact scaled-dot-product attention,
                 with the score matrix materialised, in float64.
-  tiled.py      the blockwise online-softmax forward exactly as the pages lay
-                it out, in float64, used only to cross-check the definition.
+  tiled.py      a blockwise online-softmax route to the same result (partial
+                summaries of key blocks, combined in any grouping), in
+                float64, used only to cross-check the definition.
   backward.py   the gradients dQ, dK, dV of the definition (chain rule through
                 the softmax), with P materialised, in float64.
   padding.py    attention over a padded batch with a key padding mask: remove

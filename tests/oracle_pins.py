@@ -73,7 +73,7 @@ def pin_brute_force(fn):
 
 
 # ---------------------------------------------------------------------------
-# 2. The pages' blockwise online algorithm gives the same O and L.
+# 2. The blockwise online-softmax route (any grouping of key blocks) gives the same O and L.
 # ---------------------------------------------------------------------------
 
 def pin_tiled_agrees(fn):
@@ -86,7 +86,7 @@ def pin_tiled_agrees(fn):
         scale = 1 / math.sqrt(d)
         O, L = fn(q, k, v, scale, causal)
         for br, bc in [(1, 1), (3, 16), (16, 3), (16, 16), (64, 7)]:
-            for form in ("local", "running"):
+            for form in ("local", "tree", "running"):
                 Ot, Lt = attention_tiled(q, k, v, scale, causal, br, bc, form)
                 _close(O, Ot, 1e-12, f"O tiled br={br} bc={bc} {form}")
                 _close(L, Lt, 1e-12, f"L tiled br={br} bc={bc} {form}")
@@ -360,7 +360,8 @@ def pin_band_tiled_agrees(fn):
         v = rng.standard_normal((Nk, 3))
         for window in ((None, 0), (4, 3), (0, 6), (7, None)):
             O, L = fn(q, k, v, 0.6, window)
-            for br, bc, form in ((1, 1, "local"), (4, 3, "local"), (16, 16, "running")):
+            for br, bc, form in ((1, 1, "local"), (4, 3, "local"), (3, 2, "tree"),
+                                 (16, 16, "running")):
                 Ot, Lt = attention_tiled(q, k, v, 0.6, False, br, bc, form, window=window)
                 _close(O, Ot, 1e-12, f"O tiled band {window} {br}x{bc} {form}")
                 _close_inf(L, Lt, 1e-12, f"L tiled band {window} {br}x{bc} {form}")
