@@ -68,17 +68,47 @@ def _dtype_code(dtype):
     raise TypeError(f"q, k, v must be bfloat16 or float16 (got {dtype})")
 
 
+def _on_gpu(t) -> bool:
+    return t.device.type == "cuda"
+
+
 def _check_tensor(t, name, ndim):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     _dtype_code(t.dtype)
-    if t.device.type != "cuda":
+    if not _on_gpu(t):
         raise ValueError(f"{name} must be on a GPU device (got {t.device})")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
     if t.shape[-1] > 1 and t.stride(-1) != 1:
         raise ValueError(f"{name} must have a contiguous last (head) dimension")
+
+
+def _same_device(q, *named):
+    """Every (tensor, name) pair lives on q's device (the kernels get raw pointers)."""
+    for t, n in named:
+        if t.device != q.device:
+            raise ValueError(f"{n} must be on q's device {q.device} (got {t.device})")
+
+
+def _check_aux(t, name, q, shape, dtype, contiguous=True, dtype_error=ValueError):
+    """An output or auxiliary tensor the caller passes: a torch.Tensor on q's GPU
+    device, of the given shape and dtype, contiguous unless told otherwise. Checked
+    before any library call, so a host tensor raises here instead of reaching a
+    kernel as a host pointer."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not _on_gpu(t) or t.device != q.device:
+        raise ValueError(f"{name} must be on q's device {q.device} (got {t.device})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.dtype != dtype:
+        raise dtype_error(f"{name} must be {dtype} (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
 
 
 def _strides(t):
@@ -93,14 +123,20 @@ def _plain(*ts):
     return all(t.is_contiguous() and t.dtype == torch.bfloat16 for t in ts)
 
 
-def _out(out, like, shape, name):
+def _out(out, like, shape, name, contiguous=False):
     torch = _torch()
     if out is None:
         return torch.empty(shape, dtype=like.dtype, device=like.device)
     _check_tensor(out, name, len(shape))
-    if tuple(out.shape) != tuple(shape) or out.dtype != like.dtype:
-        raise ValueError(f"{name} must have shape {tuple(shape)} and dtype {like.dtype}")
+    _check_aux(out, name, like, shape, like.dtype, contiguous=contiguous)
     return out
+
+
+def _lse(lse, q, shape, name="lse"):
+    torch = _torch()
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=q.device)
+    return _check_aux(lse, name, q, shape, torch.float32)
 
 
 def _scale(softmax_scale, d):
@@ -137,10 +173,7 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, window
         raise ValueError("q, k and v must be on the same device")
     Nk = k.shape[1]
     out = _out(out, q, (B, Nq, H, d), "out")
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, Nq)")
+    lse = _lse(lse, q, (B, H, Nq))
     scale = _scale(softmax_scale, d)
     wl, wr = (-1, -1) if window is None else _window(window, causal)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
@@ -186,15 +219,13 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=Fa
         raise ValueError("q, k and v must share the packed shape (total, H, d)")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError(f"q, k and v must share one dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
+    _same_device(q, (k, "k"), (v, "v"))
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
             or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
     num_seqs = cu_seqlens.numel() - 1
     out = _out(out, q, (total, H, d), "out")
-    if lse is None:
-        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape (H, total)")
+    lse = _lse(lse, q, (H, total))
     scale = _scale(softmax_scale, d)
     wl, wr = (-1, -1) if window is None else _window(window, causal)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -236,18 +267,13 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != d \
             or o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("shape mismatch among q, k, v, o and dout")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if delta is None:
-        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _check_contiguous((q, k, v, o, dout, dq, dk, dv), ("q", "k", "v", "o", "dout", "dq", "dk", "dv"),
-                      q.dtype)
-    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
-        raise ValueError("dq, dk and dv must be shaped like q, k and v")
-    for t, n in ((lse, "lse"), (delta, "delta")):
-        if t.shape != (B, H, Nq) or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{n} must be a contiguous float32 tensor of shape (B, H, Nq)")
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"))
+    _check_contiguous((q, k, v, o, dout), ("q", "k", "v", "o", "dout"), q.dtype)
+    dq, dk, dv = (torch.empty_like(x) if g is None else
+                  _check_aux(g, n, q, x.shape, q.dtype, dtype_error=TypeError)
+                  for g, x, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")))
+    _check_aux(lse, "lse", q, (B, H, Nq), torch.float32)
+    delta = _lse(delta, q, (B, H, Nq), "delta")
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
     dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
@@ -287,21 +313,16 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=N
     total, H, d = q.shape
     if any(t.shape != q.shape for t in (k, v, o, dout)):
         raise ValueError("q, k, v, o and dout must share the packed shape (total, H, d)")
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"))
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
             or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if delta is None:
-        delta = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    _check_contiguous((q, k, v, o, dout, dq, dk, dv), ("q", "k", "v", "o", "dout", "dq", "dk", "dv"),
-                      q.dtype)
-    if any(t.shape != q.shape for t in (dq, dk, dv)):
-        raise ValueError("dq, dk and dv must be shaped like q")
-    for t, n in ((lse, "lse"), (delta, "delta")):
-        if t.shape != (H, total) or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{n} must be a contiguous float32 tensor of shape (H, total)")
+    _check_contiguous((q, k, v, o, dout), ("q", "k", "v", "o", "dout"), q.dtype)
+    dq, dk, dv = (torch.empty_like(q) if g is None else
+                  _check_aux(g, n, q, q.shape, q.dtype, dtype_error=TypeError)
+                  for g, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    _check_aux(lse, "lse", q, (H, total), torch.float32)
+    delta = _lse(delta, q, (H, total), "delta")
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens.data_ptr())
     dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
@@ -381,16 +402,12 @@ def fa_fwd_local(q, k, v, n_global, map_w, window, softmax_scale=None, causal=Fa
                          f"k {tuple(k.shape)} v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
+    _same_device(q, (k, "k"), (v, "v"))
     if not all(t.is_contiguous() for t in (q, k, v)):
         raise ValueError("q, k and v must be contiguous")
     win_rows, win_cols = (int(w) for w in window)
-    out = _out(out, q, (B, N, H, d), "out")
-    if not out.is_contiguous():
-        raise ValueError("out must be contiguous")
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, N)")
+    out = _out(out, q, (B, N, H, d), "out", contiguous=True)
+    lse = _lse(lse, q, (B, H, N))
     clamp = lambda x: max(min(int(x), 2**31 - 1), -1)  # noqa: E731 - sizes beyond int32 mean no bound
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -416,24 +433,22 @@ def fa_decode(q, k, v, seqlens_k=None, softmax_scale=None, out=None, lse=None, w
                          f"k {tuple(k.shape)} v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
+    _same_device(q, (k, "k"), (v, "v"))
     if not all(t.is_contiguous() for t in (q, k, v)):
         raise ValueError("q, k and v must be contiguous for the decode")
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like q")
-    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H)")
+    out = _out(out, q, tuple(q.shape), "out", contiguous=True)
+    lse = _lse(lse, q, (B, H))
     sl = 0
     if seqlens_k is not None:
-        if not isinstance(seqlens_k, torch.Tensor) or seqlens_k.dtype != torch.int32 \
-                or tuple(seqlens_k.shape) != (B,) or seqlens_k.device != q.device:
-            raise ValueError("seqlens_k must be an int32 tensor of shape (B,) on q's device")
+        _check_aux(seqlens_k, "seqlens_k", q, (B,), torch.int32)
         sl = seqlens_k.data_ptr()
     need = decode_workspace_bytes(B, Nk, H, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        if not isinstance(workspace, torch.Tensor) or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        _check_aux(workspace, "workspace", q, (workspace.numel(),), torch.uint8)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         check(raw_fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

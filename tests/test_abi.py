@@ -487,3 +487,101 @@ def test_bwd_local_argument_checks():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         assert lib.raw_fa_bwd_local(*args, 2, 408, 2, 64, bf, 0.1, 1, 8, 20, 2, 2, None) == HIP
+
+
+# ---------------------------------------------------------------------------
+# Outputs and auxiliary tensors on another device than q are refused by the
+# binding before any library call (a host pointer must never reach a kernel).
+# The host stands in for "q's GPU" here: _on_gpu is patched to accept CPU
+# tensors, and "meta" tensors play a tensor on another device.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def host_as_gpu(monkeypatch):
+    torch = pytest.importorskip("torch")
+    monkeypatch.setattr(aa, "_on_gpu", lambda t: t.device.type == "cpu")
+
+    def refuse(*a, **k):
+        raise AssertionError("a library call was reached")
+    for name in dir(aa):
+        if name.startswith("raw_fa_"):
+            monkeypatch.setattr(aa, name, refuse)
+    return torch
+
+
+def _meta(torch, shape, dtype):
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+def test_forward_outputs_on_another_device_are_refused(host_as_gpu):
+    torch = host_as_gpu
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(1, 8, 2, 32, dtype=bf)
+    with pytest.raises(ValueError, match="^out must be on"):
+        aa.fa_fwd(q, q, q, out=_meta(torch, (1, 8, 2, 32), bf))
+    with pytest.raises(ValueError, match="^lse must be on"):
+        aa.fa_fwd(q, q, q, lse=_meta(torch, (1, 2, 8), f32))
+    with pytest.raises(ValueError, match="^lse must be contiguous"):  # strided lse
+        aa.fa_fwd(q, q, q, lse=torch.zeros(1, 8, 2, dtype=f32).transpose(1, 2))
+    with pytest.raises(ValueError, match="^k must be on"):
+        aa.fa_fwd(q, _meta(torch, (1, 8, 2, 32), bf), q)
+    qv = torch.zeros(8, 2, 32, dtype=bf)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="^v must be on"):
+        aa.fa_fwd_varlen(qv, qv, _meta(torch, (8, 2, 32), bf), cu, 8)
+    with pytest.raises(ValueError, match="^lse must be on"):
+        aa.fa_fwd_varlen(qv, qv, qv, cu, 8, lse=_meta(torch, (2, 8), f32))
+    with pytest.raises(ValueError, match="^out must be on"):
+        aa.fa_fwd_varlen(qv, qv, qv, cu, 8, out=_meta(torch, (8, 2, 32), bf))
+    with pytest.raises(ValueError, match="^lse must be on"):
+        aa.fa_fwd_local(q, q, q, 2, 3, (1, 1), lse=_meta(torch, (1, 2, 8), f32))
+    with pytest.raises(ValueError, match="^out must be on"):
+        aa.fa_fwd_local(q, q, q, 2, 3, (1, 1), out=_meta(torch, (1, 8, 2, 32), bf))
+
+
+@pytest.mark.parametrize("name", ["lse", "delta", "dq", "dk", "dv", "o", "dout"])
+def test_backward_tensors_on_another_device_are_refused(host_as_gpu, name):
+    torch = host_as_gpu
+    bf, f32 = torch.bfloat16, torch.float32
+    x = torch.zeros(1, 8, 2, 32, dtype=bf)
+    kw = dict(q=x, k=x, v=x, o=x, lse=torch.zeros(1, 2, 8, dtype=f32), dout=x)
+    extra = {}
+    meta = _meta(torch, (1, 2, 8), f32) if name in ("lse", "delta") else \
+        _meta(torch, (1, 8, 2, 32), bf)
+    if name in ("lse", "o", "dout"):
+        kw[name] = meta
+    else:
+        extra[name] = meta
+    with pytest.raises(ValueError, match=f"^{name} must be on"):
+        aa.fa_bwd(kw["q"], kw["k"], kw["v"], kw["o"], kw["lse"], kw["dout"], **extra)
+    # the same through the packed entry point
+    xv = torch.zeros(8, 2, 32, dtype=bf)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    kw = dict(q=xv, k=xv, v=xv, o=xv, lse=torch.zeros(2, 8, dtype=f32), dout=xv)
+    extra = {}
+    meta = _meta(torch, (2, 8), f32) if name in ("lse", "delta") else _meta(torch, (8, 2, 32), bf)
+    if name in ("lse", "o", "dout"):
+        kw[name] = meta
+    else:
+        extra[name] = meta
+    with pytest.raises(ValueError, match=f"^{name} must be on"):
+        aa.fa_bwd_varlen(kw["q"], kw["k"], kw["v"], kw["o"], kw["lse"], kw["dout"], cu, 8, **extra)
+
+
+def test_decode_tensors_on_another_device_or_strided_are_refused(host_as_gpu):
+    torch = host_as_gpu
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(2, 1, 4, 64, dtype=bf)
+    kv = torch.zeros(2, 100, 4, 64, dtype=bf)
+    with pytest.raises(ValueError, match="^out must be on"):
+        aa.fa_decode(q, kv, kv, out=_meta(torch, (2, 1, 4, 64), bf))
+    with pytest.raises(ValueError, match="^lse must be on"):
+        aa.fa_decode(q, kv, kv, lse=_meta(torch, (2, 4), f32))
+    with pytest.raises(ValueError, match="^workspace must be on"):
+        aa.fa_decode(q, kv, kv, workspace=_meta(torch, (1 << 20,), torch.uint8))
+    with pytest.raises(ValueError, match="^seqlens_k must be on"):
+        aa.fa_decode(q, kv, kv, seqlens_k=_meta(torch, (2,), torch.int32))
+    with pytest.raises(ValueError, match="^seqlens_k must be contiguous"):  # a strided view
+        aa.fa_decode(q, kv, kv, seqlens_k=torch.zeros(4, dtype=torch.int32)[::2])
+    with pytest.raises(ValueError, match="^seqlens_k must be torch.int32"):  # wrong dtype
+        aa.fa_decode(q, kv, kv, seqlens_k=torch.zeros(2, dtype=torch.int64))
