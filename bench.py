@@ -36,9 +36,127 @@ METRIC_BWD = "attention bwd TFLOPS (bf16) and % of MFMA peak"
 METRIC_DECODE = "attention decode HBM GB/s (bf16, one query per head)"
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_SCLK_MHZ = 2400.0             # the shader clock that peak is quoted at
 KERNEL_SOURCES = [os.path.join(ROOT, "aware_attention_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
+
+
+class ClockSampler:
+    """Samples the GPU's shader (GFX) clock through the amdsmi library in a
+    background thread, with host timestamps. The SMU refreshes these metrics
+    about once a second (measured on MI355X: the readings stay constant for
+    ~1 s), so a reading is only meaningful once a refresh has happened under
+    load; `sustained` reports the last refresh seen in a window. Silent (no
+    samples) where amdsmi or the metric is unavailable."""
+
+    def __init__(self, period_s: float = 0.005):
+        import threading
+        self.period_s = period_s
+        self.samples = []          # (perf_counter, MHz)
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = self._open()
+
+    def _open(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+        except Exception:   # noqa: BLE001 - no SMI library or no access: no samples
+            return None
+        if not handles:
+            return None
+        handle = handles[0]
+        if len(handles) > 1:   # the device torch uses, by PCI bus
+            try:
+                import torch
+                bus = torch.cuda.get_device_properties(0).pci_bus_id
+                for h in handles:
+                    if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                        handle = h
+            except Exception:   # noqa: BLE001
+                pass
+
+        def from_metrics():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            vals = m.get("current_gfxclks")
+            if isinstance(vals, (list, tuple)):
+                vals = [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
+                if vals:
+                    return sum(vals) / len(vals)
+            x = m.get("current_gfxclk")
+            return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+
+        def from_clock_info():
+            x = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX).get("clk")
+            return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+
+        for name, fn in (("amdsmi gpu_metrics current_gfxclks (mean over XCDs)", from_metrics),
+                         ("amdsmi clock_info GFX", from_clock_info)):
+            try:
+                if fn() is not None:
+                    self.source = name
+                    return fn
+            except Exception:   # noqa: BLE001
+                continue
+        return None
+
+    def start(self):
+        import threading
+        if self._read is None:
+            return self
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    mhz = self._read()
+                except Exception:   # noqa: BLE001
+                    mhz = None
+                if mhz is not None:
+                    self.samples.append((time.perf_counter(), mhz))
+                self._stop.wait(self.period_s)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def sustained(self, t_load: float, t1: float):
+        """The clock of the last metrics refresh observed in (t_load, t1]: a
+        reading that differs from the one current when the load started at
+        t_load. Returns (MHz, seconds before t1 it was first seen), or
+        (None, None) if no refresh happened under load."""
+        before = [mhz for t, mhz in self.samples if t <= t_load]
+        prev = before[-1] if before else None
+        last = None
+        for t, mhz in self.samples:
+            if t_load < t <= t1 and mhz != prev:
+                last, prev = (mhz, t), mhz
+        if last is None:
+            return None, None
+        return last[0], t1 - last[1]
+
+
+def host_cores() -> dict:
+    """Host CPU figures for the baseline: logical CPUs, the affinity set and the
+    threads the BLAS library runs with."""
+    info = {"cpu_count": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["affinity"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_threads"] = max([i.get("num_threads", 1) for i in threadpool_info()
+                                    if i.get("user_api") == "blas"] or [None])
+    except Exception:   # noqa: BLE001
+        info["blas_threads"] = None
+    return info
 
 
 def kernel_digest() -> str:
@@ -115,7 +233,7 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0):
         sample = f"{heads} (sequence, head) pairs of {spec.num_seqs * spec.H}"
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "sample": sample + f"; float64 numpy, {dt:.1f} s"}
+            "kind": "oracle", "sample": sample + f"; float64 numpy, {dt:.1f} s", **host_cores()}
 
 
 def cpu_baseline_bwd(wl: dict, budget_s: float = 12.0):
@@ -156,7 +274,7 @@ def cpu_baseline_bwd(wl: dict, budget_s: float = 12.0):
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": f"{heads} of {spec.B * spec.H} (batch, head) pairs, "
-                                        f"backward, float64 numpy, {dt:.1f} s"}
+                                        f"backward, float64 numpy, {dt:.1f} s", **host_cores()}
 
 
 def cpu_baseline_decode(wl: dict, budget_s: float = 12.0):
@@ -176,9 +294,11 @@ def cpu_baseline_decode(wl: dict, budget_s: float = 12.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": done * per_head / dt / 1e9, "unit": "GB/s", "cores": os.cpu_count() or 1,
+    hc = host_cores()
+    return {"value": done * per_head / dt / 1e9, "unit": "GB/s",
+            "cores": int(hc["blas_threads"] or hc["cpu_count"] or 1),
             "kind": "oracle", "sample": f"{done} of {spec.B * spec.H} (batch, head) rows, "
-                                        f"float64 numpy, {dt:.1f} s"}
+                                        f"float64 numpy, {dt:.1f} s", **hc}
 
 
 def main():
@@ -186,6 +306,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--min-warmup-s", type=float, default=1.2,
+                    help="after the --warmup steps, keep running untimed steps until the "
+                         "warm-up has lasted this long: the shader clock settles under load "
+                         "over tens of milliseconds (the first launches run up to 15%% slower), "
+                         "and the SMU's clock reading refreshes about once a second")
     ap.add_argument("--workload", default="prefill8k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
@@ -289,9 +414,18 @@ def main():
             aa.fa_fwd_varlen(q, k, v, cu, wl["max_seqlen"], softmax_scale=spec.scale,
                              causal=spec.causal, out=o, lse=lse)
 
+    clock = ClockSampler().start()
+    tw = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    warm_launches = args.warmup
+    while time.perf_counter() - tw < args.min_warmup_s:
+        for _ in range(8):
+            step()
+        warm_launches += 8
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - tw
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -300,7 +434,13 @@ def main():
         step()
     end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    clock.stop()
+    sclk, sclk_age = clock.sustained(tw + 0.05, t1)
+    sclk_info = {"sclk_mhz": None if sclk is None else round(sclk, 1),
+                 "sclk_age_s": None if sclk_age is None else round(sclk_age, 3),
+                 "sclk_source": clock.source}
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -319,6 +459,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
             "tflops": round(tflops, 2), "wall_s_timed": round(wall, 4),
+            "warmup_launches": warm_launches, "warmup_s": round(warm_s, 3), **sclk_info,
         }
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_decode(wl)
@@ -348,7 +489,14 @@ def main():
         },
         "kernel_digest": kernel_digest(),
         "wall_s_timed": round(wall, 4),
+        "warmup_launches": warm_launches,
+        "warmup_s": round(warm_s, 3),
+        **sclk_info,
     }
+    if sclk is not None:   # the dense bf16 peak scales with the shader clock (2.5 PF at 2.4 GHz)
+        peak_at = PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_MHZ
+        out["peak_at_sclk_tflops"] = round(peak_at, 1)
+        out["frac_at_sclk"] = round(tflops / peak_at, 4)
     if args.backward:
         config["pass"] = "backward"
     if not args.no_cpu_baseline:
