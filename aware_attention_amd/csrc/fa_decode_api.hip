@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "fa.h"
@@ -57,23 +58,11 @@ hipError_t launch_decode(const fa::DecodeParams& p, int d, hipStream_t stream) {
   }
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d) {
-  if (B < 1 || Nk < 1 || H < 1 || d < 1) return 0;
-  const Plan s = plan(B, Nk, H);
-  return (size_t)B * H * s.splits * ((size_t)d + 1) * sizeof(float);
-}
-
-fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                    const int32_t* seqlens_k, int32_t B, int32_t Nk, int32_t H, int32_t d,
-                    int32_t dtype, float softmax_scale, void* workspace, size_t workspace_bytes,
-                    void* stream) {
-  fa_host::g_last_error.clear();
-  if (!q || !k || !v || !o || !lse || !workspace)
-    return fail(FA_ERR_INVALID_ARGUMENT, "null tensor or workspace pointer");
+// Checks shared by both decode entry points (everything but the workspace).
+fa_status check_decode_args(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const int32_t* seqlens_k, int32_t B, int32_t Nk,
+                            int32_t H, int32_t d, int32_t dtype, float softmax_scale) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (B < 1 || Nk < 1 || H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B, Nk and H must be >= 1");
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
@@ -81,16 +70,18 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   if (d != 32 && d != 64 && d != 128 && d != 256)
     return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64, 128 or 256");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return fail(FA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned (seqlens_k 4-byte)");
-  const size_t need = fa_decode_workspace_bytes(B, Nk, H, d);
-  if (workspace_bytes < need)
-    return fail(FA_ERR_INVALID_ARGUMENT, "workspace smaller than fa_decode_workspace_bytes()");
   const Plan s = plan(B, Nk, H);
   if ((int64_t)B * H * s.splits > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many chunks for one launch");
-  fa_status st = check_device();
-  if (st != FA_OK) return st;
+  return FA_OK;
+}
 
+// Both launches with the partial results at `workspace` (checked by the caller).
+fa_status run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* seqlens_k, int32_t B, int32_t Nk, int32_t H, int32_t d,
+                     int32_t dtype, float softmax_scale, void* workspace, void* stream) {
+  const Plan s = plan(B, Nk, H);
   fa::DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -113,6 +104,95 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                            : launch_decode<false>(p, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return FA_OK;
+}
+
+// ---- the library-held scratch of fa_decode_noalloc ----
+// One array per GPU, in device memory the code object reserves when it is
+// loaded on that GPU (no allocation call), held until the process ends. Host
+// code never uses the array's name as an address: the device address of this
+// GPU's copy comes from hipGetSymbolAddress, looked up once per device (with
+// that device current) and kept in g_scratch_addr.
+constexpr size_t kNoAllocScratchBytes = FA_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// This device's address of `scratch` (nullptr and the error recorded on failure).
+void* scratch_address(fa_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = fail(FA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kScratchDevices) {
+    *st = fail(FA_ERR_UNSUPPORTED, "device ordinal out of range");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *st = fail(FA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                 (e != hipSuccess ? hipGetErrorString(e) : "null address"));
+      return nullptr;
+    }
+    g_scratch_addr[dev] = ptr;
+  }
+  *st = FA_OK;
+  return g_scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d) {
+  if (B < 1 || Nk < 1 || H < 1 || d < 1) return 0;
+  const Plan s = plan(B, Nk, H);
+  return (size_t)B * H * s.splits * ((size_t)d + 1) * sizeof(float);
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* seqlens_k, int32_t B, int32_t Nk, int32_t H, int32_t d,
+                    int32_t dtype, float softmax_scale, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  fa_host::g_last_error.clear();
+  if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "null workspace pointer");
+  fa_status st = check_decode_args(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (workspace_bytes < fa_decode_workspace_bytes(B, Nk, H, d))
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace smaller than fa_decode_workspace_bytes()");
+  st = check_device();
+  if (st != FA_OK) return st;
+  return run_decode(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, softmax_scale, workspace, stream);
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* seqlens_k, int32_t B, int32_t Nk, int32_t H,
+                            int32_t d, int32_t dtype, float softmax_scale, void* stream) {
+  fa_host::g_last_error.clear();
+  fa_status st = check_decode_args(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_bytes(B, Nk, H, d);
+  if (need > kNoAllocScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED, "these sizes need " + std::to_string(need) +
+                                        " bytes of partial results, above the " +
+                                        std::to_string(kNoAllocScratchBytes) +
+                                        " bytes fa_decode_noalloc holds; use fa_decode");
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* ws = scratch_address(&st);
+  if (!ws) return st;
+  return run_decode(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, softmax_scale, ws, stream);
 }
 
 }  // extern "C"

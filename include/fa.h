@@ -274,6 +274,28 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
 /* Workspace bytes fa_decode needs for these sizes (0 for sizes below 1). */
 size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d);
 
+/* Bytes of the scratch array fa_decode_noalloc holds on each GPU. */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation calls. Same arguments and results as
+ * fa_decode minus the workspace; the partial results go to a scratch array
+ * of FA_DECODE_NOALLOC_SCRATCH_BYTES (8 MiB) that the library's code object
+ * reserves on each GPU it runs on, held until the process ends. The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a device looks the array's address up once.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (each call overwrites every part it reads, so nothing needs
+ * clearing): calls that overlap on one GPU (other streams, other threads)
+ * race. Errors: as fa_decode; sizes whose partial results
+ * (fa_decode_workspace_bytes) exceed the array are FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* seqlens_k, int32_t B, int32_t Nk, int32_t H,
+                            int32_t d, int32_t dtype, float softmax_scale, void* stream);
+
 /*
  * Local window on a token map plus global anchor tokens (self-attention):
  * the detector's mix of local-window attention and a few global tokens

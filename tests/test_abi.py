@@ -585,3 +585,45 @@ def test_decode_tensors_on_another_device_or_strided_are_refused(host_as_gpu):
         aa.fa_decode(q, kv, kv, seqlens_k=torch.zeros(4, dtype=torch.int32)[::2])
     with pytest.raises(ValueError, match="^seqlens_k must be torch.int32"):  # wrong dtype
         aa.fa_decode(q, kv, kv, seqlens_k=torch.zeros(2, dtype=torch.int64))
+
+
+# ---------------------------------------------------------------------------
+# fa_decode_noalloc: the decode without a workspace argument (host checks)
+# ---------------------------------------------------------------------------
+
+def _decode_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, sl=None, B=2, Nk=1000, H=4, d=128,
+             dtype=_lib.FA_DTYPE_BF16, scale=0.088, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["sl"], a["B"],
+                                      a["Nk"], a["H"], a["d"], a["dtype"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(lse=None), INV), (dict(B=0), INV), (dict(Nk=0), INV),
+    (dict(dtype=5), INV), (dict(scale=float("inf")), INV), (dict(o=P + 8), INV),
+    (dict(sl=P + 2), INV), (dict(d=48), UNS),
+    # partial results above the 8 MiB array: 8192 (batch, head) pairs at d = 256,
+    # and one pair over a cache split into 9766 chunks of 4096 keys
+    (dict(B=64, H=128, Nk=100, d=256), UNS), (dict(B=1, H=1, Nk=40_000_000, d=256), UNS),
+])
+def test_fa_decode_noalloc_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_limit_matches_the_workspace_plan():
+    _lib_or_skip()
+    lim = _lib.FA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert "FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)" in open(HEADER).read()
+    assert _lib.decode_workspace_bytes(64, 100, 128, 256) > lim
+    assert _lib.decode_workspace_bytes(16, 32768, 32, 256) <= lim   # the decode workloads fit
+
+
+def test_decode_noalloc_valid_call_without_a_device_is_a_hip_error():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _decode_noalloc() == HIP
+    assert _decode_noalloc(d=32, sl=P, dtype=_lib.FA_DTYPE_F16) == HIP
