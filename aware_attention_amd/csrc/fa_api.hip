@@ -200,7 +200,6 @@ fa_status check_dtype(int32_t dtype) {
 fa_status check_common(int32_t H, int32_t d, float scale) {
   if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
   if (d != 32 && d != 64 && d != 128 && d != 256)
     return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64, 128 or 256");
   return FA_OK;
@@ -261,7 +260,8 @@ fa_status dense_fwd(const void* q, const void* k, const void* v, void* o, float*
   p.H = H;
   p.nbatch = B;
   p.n_qtiles = (int32_t)n_qt;
-  p.scale_log2 = softmax_scale * kLog2e;
+  p.scale_log2 = std::fabs(softmax_scale) * kLog2e;
+  p.q_sign = softmax_scale < 0.f ? 0x80008000u : 0u;
   p.win_left = window_side(win_left, Nq, Nk);
   p.win_right = window_side(win_right, Nq, Nk);
   p.band_off = Nk - Nq;
@@ -319,7 +319,8 @@ fa_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float
   p.H = H;
   p.nbatch = num_seqs;
   p.n_qtiles = (int32_t)n_qt;
-  p.scale_log2 = softmax_scale * kLog2e;
+  p.scale_log2 = std::fabs(softmax_scale) * kLog2e;
+  p.q_sign = softmax_scale < 0.f ? 0x80008000u : 0u;
   p.win_left = window_side(win_left, max_seqlen, max_seqlen);
   p.win_right = window_side(win_right, max_seqlen, max_seqlen);
   p.band_off = 0;

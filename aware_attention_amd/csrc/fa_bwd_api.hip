@@ -113,7 +113,6 @@ fa_status check_bwd_common(int32_t H, int32_t d, int32_t dtype, float scale, int
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
   if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
   return FA_OK;
 }

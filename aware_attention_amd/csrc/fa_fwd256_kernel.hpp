@@ -91,6 +91,10 @@ void fwd256_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
+  if (p.q_sign) {   // negative scale: scale q.k = |scale| (-q).k
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qr[s]) ^ p.q_sign);
+  }
   const BwdLanes<D> ln(lane);
   f32x16 o[DB];
 #pragma unroll

@@ -95,7 +95,11 @@ struct FwdParams {
   int32_t H;
   int32_t nbatch;              // B (dense) or num_seqs (varlen)
   int32_t n_qtiles;            // query tiles per (batch or sequence, head)
-  float scale_log2;            // softmax_scale * log2(e), >= 0
+  float scale_log2;            // |softmax_scale| * log2(e)
+  // 0, or 0x80008000 for a negative softmax_scale: the sign is moved into Q
+  // (every 16-bit element of the Q registers negated, which is exact), so the
+  // kernel always works with the non-negative |scale| above.
+  uint32_t q_sign;
   // Band (BAND instances only): query i sees key j iff
   // i + band_off - win_left <= j <= i + band_off + win_right.
   int32_t win_left;            // >= 0; an unbounded side is passed as max(Nq, Nk)
@@ -434,6 +438,10 @@ void fwd_kernel(FwdParams p) {
   } else {
 #pragma unroll
     for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  if (p.q_sign) {   // negative scale: scale q.k = |scale| (-q).k
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qr[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qr[s]) ^ p.q_sign);
   }
 
   // ---- direct HBM -> LDS copies, issued by the waves of group A ----

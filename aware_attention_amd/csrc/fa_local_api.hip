@@ -52,7 +52,6 @@ fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, flo
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
   if (!std::isfinite(softmax_scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  if (softmax_scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
   if (n_global < 0 || map_w < 1 || win_rows < 0 || win_cols < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "need n_global >= 0, map_w >= 1, win_rows >= 0, win_cols >= 0");
   if (d != 32 && d != 64 && d != 128 && d != 256)

@@ -29,7 +29,8 @@
  *     *_strided entry points say so; L is float32.
  *   - Head dimension d must be 32, 64, 128 or 256 in the forward entry
  *     points (every mask), 32, 64 or 128 in the backward.
- *   - softmax_scale must be finite and >= 0 (callers normally pass 1/sqrt(d)).
+ *   - softmax_scale may be any finite value, 0 and negative values included
+ *     (callers normally pass 1/sqrt(d)); L is computed on the scaled scores.
  *   - causal = 1 applies the lower-triangular mask of self-attention (query i
  *     sees keys j <= i) and needs as many queries as keys; causal = 0 is
  *     unmasked attention.

@@ -46,8 +46,9 @@ def d_rounding_terms(qf, kf, vf, dof, scale, causal, eps, window=None, P=None):
         P = attention_probs(qf, kf, scale, causal, window=window)
     O = P @ vf
     dD = eps * np.sum(np.abs(dof * O), axis=1)                       # (Nq,)
-    tq = scale * dD[:, None] * (P @ np.abs(kf))                      # (Nq, d)
-    tk = scale * (P.T @ (dD[:, None] * np.abs(qf)))                  # (Nk, d)
+    # bounds on magnitudes: the scale enters with its absolute value
+    tq = abs(scale) * dD[:, None] * (P @ np.abs(kf))                 # (Nq, d)
+    tk = abs(scale) * (P.T @ (dD[:, None] * np.abs(qf)))             # (Nk, d)
     return tq, tk, dD
 
 
@@ -101,13 +102,13 @@ def _np(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def check_bwd_dense(B, Nq, Nk, H, d, causal, seed, dtype="bf16"):
+def check_bwd_dense(B, Nq, Nk, H, d, causal, seed, dtype="bf16", scale=None):
     import aware_attention_amd as aa
     torch = torch_or_skip()
     say(f"bwd dense B={B} Nq={Nq} Nk={Nk} H={H} d={d} causal={causal} dtype={dtype} seed={seed}")
     q, k, v = W.make_dense(B, Nq, H, d, seed, Nk=Nk, dtype=dtype)
     do, _, _ = W.make_dense(B, Nq, H, d, seed + 1, dtype=dtype)
-    scale = 1 / np.sqrt(d)
+    scale = 1 / np.sqrt(d) if scale is None else scale
     qf, kf, vf, dof = (to_f64(x, dtype) for x in (q, k, v, do))
     oref, lref = attention_dense(qf, kf, vf, scale, causal)
     dq, dk, dv, delta = aa.fa_bwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
@@ -117,7 +118,7 @@ def check_bwd_dense(B, Nq, Nk, H, d, causal, seed, dtype="bf16"):
     torch.cuda.synchronize()
     gq, gk, gv, gd = attention_backward_dense(qf, kf, vf, dof, scale, causal)
     tq, tk, dD = dense_terms(qf, kf, vf, dof, scale, causal, EPS_O[dtype])
-    what = f"Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype}"
+    what = f"Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype} scale={scale}"
     assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
     assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
     assert_grad_close(_np(dv), gv, "dv " + what)

@@ -16,15 +16,16 @@ from tests.gpu_util import (assert_l_close, assert_o_close, o_to_f64, say, to_de
 pytestmark = pytest.mark.gpu
 
 
-def check_256(B, Nq, Nk, H, causal, seed, dtype="bf16"):
+def check_256(B, Nq, Nk, H, causal, seed, dtype="bf16", scale=1 / 16.0):
     import aware_attention_amd as aa
     torch = torch_or_skip()
     say(f"d256 B={B} Nq={Nq} Nk={Nk} H={H} causal={causal} {dtype} seed={seed}")
     q, k, v = W.make_dense(B, Nq, H, 256, seed, Nk=Nk, dtype=dtype)
-    o, lse = aa.fa_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), causal=causal)
+    o, lse = aa.fa_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), causal=causal,
+                       softmax_scale=scale)
     torch.cuda.synchronize()
     oref, lref = attention_dense(to_f64(q, dtype), to_f64(k, dtype), to_f64(v, dtype),
-                                 1 / 16.0, causal)
+                                 scale, causal)
     assert_o_close(o_to_f64(o), oref, f"d256 O Nq={Nq} Nk={Nk} causal={causal}")
     assert_l_close(lse.cpu().numpy().astype(np.float64), lref, f"d256 L Nq={Nq} causal={causal}")
 

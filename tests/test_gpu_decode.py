@@ -17,18 +17,19 @@ from tests.gpu_util import (L_ATOL, assert_o_close, o_to_f64, say, to_dev, to_f6
 pytestmark = pytest.mark.gpu
 
 
-def check_decode(B, Nk, H, d, seed, lens=None, dtype="bf16"):
+def check_decode(B, Nk, H, d, seed, lens=None, dtype="bf16", scale=None):
     import aware_attention_amd as aa
     torch = torch_or_skip()
     say(f"decode B={B} Nk={Nk} H={H} d={d} lens={lens} {dtype} seed={seed}")
     q = W.make_dense(B, 1, H, d, seed, dtype=dtype)[0]
     _, k, v = W.make_dense(B, Nk, H, d, seed + 1, dtype=dtype)
     sl = None if lens is None else torch.tensor(lens, dtype=torch.int32).cuda()
-    o, lse = aa.fa_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), seqlens_k=sl)
+    scale = 1 / np.sqrt(d) if scale is None else scale
+    o, lse = aa.fa_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), seqlens_k=sl,
+                          softmax_scale=scale)
     torch.cuda.synchronize()
     og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
     qf, kf, vf = to_f64(q, dtype), to_f64(k, dtype), to_f64(v, dtype)
-    scale = 1 / np.sqrt(d)
     for b in range(B):
         n = Nk if lens is None else max(0, min(lens[b], Nk))
         for h in range(H):

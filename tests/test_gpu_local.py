@@ -20,22 +20,23 @@ from tests.gpu_util import (L_ATOL, assert_o_close, o_to_f64, say, to_dev, to_f6
 pytestmark = pytest.mark.gpu
 
 
-def run_local(q, k, v, G, Wd, win, causal, dtype="bf16"):
+def run_local(q, k, v, G, Wd, win, causal, dtype="bf16", scale=None):
     import aware_attention_amd as aa
     torch = torch_or_skip()
     o, lse = aa.fa_fwd_local(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), G, Wd, win,
-                             causal=causal)
+                             softmax_scale=scale, causal=causal)
     torch.cuda.synchronize()
     return o_to_f64(o), lse.cpu().numpy().astype(np.float64)
 
 
-def check_local(B, N, H, d, G, Wd, win, causal, seed, dtype="bf16"):
+def check_local(B, N, H, d, G, Wd, win, causal, seed, dtype="bf16", scale=None):
     say(f"local B={B} N={N} H={H} d={d} G={G} map_w={Wd} win={win} causal={causal} {dtype} "
         f"seed={seed}")
     q, k, v = W.make_dense(B, N, H, d, seed, dtype=dtype)
-    og, lg = run_local(q, k, v, G, Wd, win, causal, dtype)
+    scale = 1 / np.sqrt(d) if scale is None else scale
+    og, lg = run_local(q, k, v, G, Wd, win, causal, dtype, scale)
     qf, kf, vf = to_f64(q, dtype), to_f64(k, dtype), to_f64(v, dtype)
-    oref, lref = attention_local_dense(qf, kf, vf, 1 / np.sqrt(d), G, Wd, win[0], win[1], causal)
+    oref, lref = attention_local_dense(qf, kf, vf, scale, G, Wd, win[0], win[1], causal)
     what = f"G={G} map_w={Wd} win={win} causal={causal} N={N} d={d}"
     assert_o_close(og, oref, "local O " + what)
     err = np.max(np.abs(lg - lref))

@@ -45,12 +45,12 @@ def run_padded(q, k, v, mask, scale, causal, dtype="bf16"):
     return o_to_f64(o), lse.cpu().numpy().astype(np.float64)
 
 
-def check_padded(B, S, H, d, causal, seed, dtype="bf16", mask=None):
+def check_padded(B, S, H, d, causal, seed, dtype="bf16", mask=None, scale=None):
     torch_or_skip()
     say(f"padded B={B} S={S} H={H} d={d} causal={causal} dtype={dtype} seed={seed}")
     q, k, v = W.make_dense(B, S, H, d, seed, dtype=dtype)
     mask = _masks(B, S, seed) if mask is None else mask
-    scale = 1 / np.sqrt(d)
+    scale = 1 / np.sqrt(d) if scale is None else scale
     og, lg = run_padded(q, k, v, mask, scale, causal, dtype)
     oref, lref = attention_padded(to_f64(q, dtype), to_f64(k, dtype), to_f64(v, dtype), mask,
                                   scale, causal)
