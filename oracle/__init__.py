@@ -19,6 +19,8 @@ Contents:
   local.py      attention with a local window on a token map plus global
                 anchor tokens, the score mask built from map coordinates, and
                 its gradients.
+  fp8.py        FP8 E4M3 rounding, MX block scaling (32 elements sharing a
+                power-of-two scale) and attention on the dequantised values.
 """
 from .attention import (attention, attention_probs, attention_dense,
                         attention_varlen, ORACLE_DTYPE)
