@@ -29,6 +29,11 @@ library is missing or the device is not a gfx950, calls raise.
     o, lse = fa_decode(q, k, v, seqlens_k=None, softmax_scale=None)
         one query per (batch, head), q (B,1,H,d), k/v (B,Nk,H,d) the cache, split
         over the cache and merged through the log-sum-exps (fa_decode).
+    qq, qe = mx8_quantize_qk(q); vt, vte = mx8_quantize_v(v)
+    o, lse = fa_fwd_mx8(qq, qe, kq, ke, vt, vte, softmax_scale=None, causal=False)
+        the FP8 path (d = 128): operands in the OCP MX block-scaled format (E4M3
+        bytes, one E8M0 exponent byte per 32 elements; V transposed, blocked
+        along tokens); attention_mx8(q, k, v) quantises and runs it.
 
 The default scale is 1/sqrt(d), as in the definition on "FlashAttention/zh"
 (marovi.ai wiki), section 為何標準注意力運行緩慢. Only half precision on the
@@ -46,10 +51,11 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUM
                    raw_fa_bwd_local, raw_fa_bwd_varlen_band, raw_fa_decode, raw_fa_fwd_local,
                    raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
                    raw_fa_fwd_varlen,
-                   raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided)
+                   raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided, raw_fa_fwd_mx8,
+                   raw_fa_mx8_quantize_qk, raw_fa_mx8_quantize_v, mx8_tokens_padded)
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_fwd_local", "fa_bwd", "fa_bwd_varlen", "fa_decode",
-           "attention",
+           "attention", "mx8_quantize_qk", "mx8_quantize_v", "fa_fwd_mx8", "attention_mx8",
            "FaError", "load",
            "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
 
@@ -456,3 +462,82 @@ def fa_decode(q, k, v, seqlens_k=None, softmax_scale=None, out=None, lse=None, w
                             _scale(softmax_scale, d), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), stream))
     return out, lse
+
+
+def mx8_quantize_qk(x, out=None, exponents=None):
+    """Q or K (..., d = 128) bf16/fp16, densely packed -> (E4M3 bytes like x as
+    uint8, E8M0 exponent bytes (..., d / 32)) on x's device (fa_mx8_quantize_qk)."""
+    torch = _torch()
+    _check_tensor(x, "x", x.dim())
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    shape_e = tuple(x.shape[:-1]) + (d // 32,)
+    xq = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else \
+        _check_aux(out, "out", x, tuple(x.shape), torch.uint8)
+    xe = torch.empty(shape_e, dtype=torch.uint8, device=x.device) if exponents is None else \
+        _check_aux(exponents, "exponents", x, shape_e, torch.uint8)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        check(raw_fa_mx8_quantize_qk(x.data_ptr(), _dtype_code(x.dtype), rows, d, xq.data_ptr(),
+                                     xe.data_ptr(), stream))
+    return xq, xe
+
+
+def mx8_quantize_v(v):
+    """V (B, N, H, d = 128) bf16/fp16, densely packed -> (V^T E4M3 bytes (B, H, d, Np),
+    E8M0 exponent bytes (B, H, Np / 32, d)), Np = N rounded up to a multiple of 64
+    with zero tokens (fa_mx8_quantize_v)."""
+    torch = _torch()
+    _check_tensor(v, "v", 4)
+    if not v.is_contiguous():
+        raise ValueError("v must be contiguous")
+    B, N, H, d = v.shape
+    Np = mx8_tokens_padded(N)
+    vt = torch.empty((B, H, d, Np), dtype=torch.uint8, device=v.device)
+    vte = torch.empty((B, H, Np // 32, d), dtype=torch.uint8, device=v.device)
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        check(raw_fa_mx8_quantize_v(v.data_ptr(), _dtype_code(v.dtype), B, N, H, d, vt.data_ptr(),
+                                    vte.data_ptr(), stream))
+    return vt, vte
+
+
+def fa_fwd_mx8(qq, qe, kq, ke, vt, vte, softmax_scale=None, causal=False, out=None, lse=None):
+    """FP8 attention forward on MX block-scaled operands (shapes as produced by
+    mx8_quantize_qk / mx8_quantize_v); returns (o (B, Nq, H, d) bf16, lse (B, H, Nq))."""
+    torch = _torch()
+    if not isinstance(qq, torch.Tensor) or qq.dim() != 4 or qq.dtype != torch.uint8 \
+            or not _on_gpu(qq) or not qq.is_contiguous():
+        raise ValueError("qq must be a contiguous (B, Nq, H, d) uint8 tensor on a GPU")
+    B, Nq, H, d = qq.shape
+    if not isinstance(kq, torch.Tensor) or kq.dim() != 4:
+        raise ValueError("kq must be a (B, Nk, H, d) uint8 tensor")
+    Nk = kq.shape[1]
+    Np = mx8_tokens_padded(Nk)
+    _check_aux(kq, "kq", qq, (B, Nk, H, d), torch.uint8)
+    _check_aux(qe, "qe", qq, (B, Nq, H, d // 32), torch.uint8)
+    _check_aux(ke, "ke", qq, (B, Nk, H, d // 32), torch.uint8)
+    _check_aux(vt, "vt", qq, (B, H, d, Np), torch.uint8)
+    _check_aux(vte, "vte", qq, (B, H, Np // 32, d), torch.uint8)
+    if out is None:
+        out = torch.empty((B, Nq, H, d), dtype=torch.bfloat16, device=qq.device)
+    else:
+        _check_aux(out, "out", qq, (B, Nq, H, d), torch.bfloat16)
+    lse = _lse(lse, qq, (B, H, Nq))
+    scale = _scale(softmax_scale, d)
+    with torch.cuda.device(qq.device):
+        stream = torch.cuda.current_stream(qq.device).cuda_stream
+        check(raw_fa_fwd_mx8(qq.data_ptr(), qe.data_ptr(), kq.data_ptr(), ke.data_ptr(),
+                             vt.data_ptr(), vte.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Nq,
+                             Nk, H, d, scale, int(bool(causal)), stream))
+    return out, lse
+
+
+def attention_mx8(q, k, v, softmax_scale=None, causal=False):
+    """Quantise q, k, v (B, N, H, 128) to the MX FP8 format and run fa_fwd_mx8."""
+    qq, qe = mx8_quantize_qk(q)
+    kq, ke = mx8_quantize_qk(k)
+    vt, vte = mx8_quantize_v(v)
+    return fa_fwd_mx8(qq, qe, kq, ke, vt, vte, softmax_scale=softmax_scale, causal=causal)

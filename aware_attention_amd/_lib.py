@@ -20,7 +20,8 @@ FA_DTYPE_F16 = 1
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
             "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_bwd_band",
             "fa_bwd_varlen_band", "fa_bwd_padded", "fa_decode", "fa_fwd_local", "fa_bwd_local",
-            "fa_decode_workspace_bytes", "fa_decode_noalloc", "fa_status_string",
+            "fa_decode_workspace_bytes", "fa_decode_noalloc", "fa_fwd_mx8",
+            "fa_mx8_tokens_padded", "fa_mx8_quantize_qk", "fa_mx8_quantize_v", "fa_status_string",
             "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -74,6 +75,14 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_local.restype = i32
     lib.fa_decode.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
     lib.fa_decode.restype = i32
+    lib.fa_fwd_mx8.argtypes = [vp] * 8 + [i32] * 5 + [f32, i32, vp]
+    lib.fa_fwd_mx8.restype = i32
+    lib.fa_mx8_tokens_padded.argtypes = [i32]
+    lib.fa_mx8_tokens_padded.restype = i32
+    lib.fa_mx8_quantize_qk.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
+    lib.fa_mx8_quantize_qk.restype = i32
+    lib.fa_mx8_quantize_v.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.fa_mx8_quantize_v.restype = i32
     lib.fa_decode_noalloc.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, vp]
     lib.fa_decode_noalloc.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -188,6 +197,25 @@ def raw_fa_bwd_local(q, k, v, o, dout, lse, dq, dk, dv, delta, B, N, H, d, dtype
     """Pointer-level call of fa_bwd_local; returns the status code."""
     return load().fa_bwd_local(q, k, v, o, dout, lse, dq, dk, dv, delta, B, N, H, d, dtype, scale,
                                causal, n_global, map_w, win_rows, win_cols, stream)
+
+
+def raw_fa_fwd_mx8(q, qe, k, ke, vt, vte, o, lse, B, Nq, Nk, H, d, scale, causal, stream):
+    """Pointer-level call of fa_fwd_mx8; returns the status code."""
+    return load().fa_fwd_mx8(q, qe, k, ke, vt, vte, o, lse, B, Nq, Nk, H, d, scale, causal, stream)
+
+
+def raw_fa_mx8_quantize_qk(x, dtype, rows, d, xq, xe, stream):
+    """Pointer-level call of fa_mx8_quantize_qk; returns the status code."""
+    return load().fa_mx8_quantize_qk(x, dtype, rows, d, xq, xe, stream)
+
+
+def raw_fa_mx8_quantize_v(v, dtype, B, N, H, d, vt, vte, stream):
+    """Pointer-level call of fa_mx8_quantize_v; returns the status code."""
+    return load().fa_mx8_quantize_v(v, dtype, B, N, H, d, vt, vte, stream)
+
+
+def mx8_tokens_padded(N) -> int:
+    return int(load().fa_mx8_tokens_padded(N))
 
 
 def raw_fa_decode_noalloc(q, k, v, o, lse, seqlens_k, B, Nk, H, d, dtype, scale, stream):

@@ -22,8 +22,10 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17",
 
 
 # Translation units of libfa.so: the forward entry points and host helpers,
-# the backward entry points and the decode. They compile in parallel, then link.
-SOURCES = ["fa_api.hip", "fa_bwd_api.hip", "fa_decode_api.hip", "fa_local_api.hip"]
+# the backward entry points, the decode, the local pattern and the FP8 path.
+# They compile in parallel, then link.
+SOURCES = ["fa_api.hip", "fa_bwd_api.hip", "fa_decode_api.hip", "fa_local_api.hip",
+           "fa_mx8_api.hip"]
 _NOISE = "is not a recognized feature for this target"
 
 

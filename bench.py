@@ -34,6 +34,8 @@ import workloads as W  # noqa: E402
 METRIC = "attention fwd TFLOPS (bf16) and % of MFMA peak, N=1025..8192, d=128"
 METRIC_BWD = "attention bwd TFLOPS (bf16) and % of MFMA peak"
 METRIC_DECODE = "attention decode HBM GB/s (bf16, one query per head)"
+METRIC_MX8 = "attention fwd TFLOPS (FP8 E4M3, MX block-scaled) and % of MFMA peak"
+PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 PEAK_SCLK_MHZ = 2400.0             # the shader clock that peak is quoted at
@@ -316,6 +318,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (fa_bwd: dQ, dK, dV from a seeded dO) instead of "
                          "the forward; FLOPs counted as 2.5x the forward's (five products)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward (fa_fwd_mx8) on the workload's operands quantised "
+                         "to the MX block-scaled format beforehand (d = 128 dense workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), to "
                          "calibrate HBM byte counters against a known size")
@@ -388,6 +393,26 @@ def main():
                 aa.fa_fwd_local(q, k, v, G, map_w, (wr, wc), softmax_scale=spec.scale,
                                 causal=spec.causal, out=o, lse=lse)
 
+        if args.fp8:
+            if spec.d != 128 or spec.window is not None or spec.local is not None or "mask" in wl:
+                print("--fp8 runs dense d = 128 workloads (causal or not)", file=sys.stderr)
+                sys.exit(2)
+            qq, qe = aa.mx8_quantize_qk(q)
+            kq, ke = aa.mx8_quantize_qk(k)
+            vt, vte = aa.mx8_quantize_v(v)
+            torch.cuda.synchronize()
+            tq0 = time.perf_counter()
+            for _ in range(10):
+                aa.mx8_quantize_qk(q, out=qq, exponents=qe)
+                aa.mx8_quantize_qk(k, out=kq, exponents=ke)
+                aa.mx8_quantize_v(v)
+            torch.cuda.synchronize()
+            quant_ms = (time.perf_counter() - tq0) / 10 * 1e3
+            config["operands"] = "MX FP8: E4M3 elements, one E8M0 exponent per 32 (V transposed)"
+
+            def step():  # noqa: F811 - the timed step is the FP8 forward
+                aa.fa_fwd_mx8(qq, qe, kq, ke, vt, vte, softmax_scale=spec.scale,
+                              causal=spec.causal, out=o, lse=lse)
         if args.backward:
             step()
             do = to_dev(W.make_dense(spec.B, spec.N, spec.H, spec.d, spec.seed + 1)[0])
@@ -465,8 +490,10 @@ def main():
             out["cpu_baseline"] = cpu_baseline_decode(wl)
         print(json.dumps(out), flush=True)
         return
+    fp8 = getattr(args, "fp8", False)
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     out = {
-        "metric": METRIC_BWD if args.backward else METRIC,
+        "metric": METRIC_BWD if args.backward else (METRIC_MX8 if fp8 else METRIC),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -476,16 +503,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3-mx" if fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) bf16, shapes of the workload)",
         "config": config,
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
+            "frac": round(tflops / peak, 4),
+            "traffic": None if fp8 else traffic,
         },
         "kernel_digest": kernel_digest(),
         "wall_s_timed": round(wall, 4),
@@ -493,8 +520,10 @@ def main():
         "warmup_s": round(warm_s, 3),
         **sclk_info,
     }
-    if sclk is not None:   # the dense bf16 peak scales with the shader clock (2.5 PF at 2.4 GHz)
-        peak_at = PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_MHZ
+    if fp8:
+        out["quantize_ms"] = round(quant_ms, 4)
+    if sclk is not None:   # the dense MFMA peak scales with the shader clock (quoted at 2.4 GHz)
+        peak_at = peak * sclk / PEAK_SCLK_MHZ
         out["peak_at_sclk_tflops"] = round(peak_at, 1)
         out["frac_at_sclk"] = round(tflops / peak_at, 4)
     if args.backward:

@@ -275,6 +275,52 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
 /* Workspace bytes fa_decode needs for these sizes (0 for sizes below 1). */
 size_t fa_decode_workspace_bytes(int32_t B, int32_t Nk, int32_t H, int32_t d);
 
+/*
+ * FP8 forward on block-scaled operands ("FlashAttention/zh" (marovi.ai
+ * wiki), section 變體與後續版本: the FP8 generation with block scaling; section
+ * 局限性: low precision needs careful scaling). The block-scaled format is
+ * OCP MX: 32 consecutive elements share one power-of-two scale stored as an
+ * E8M0 byte (value 2^(byte - 127)); the elements are FP8 E4M3 ("fn": bias 7,
+ * largest magnitude 448, subnormals down to 2^-9) bytes. A block's exponent
+ * is floor(log2(max |x|)) - 8 clamped to [-127, 127] (an all-zero block gets
+ * -127); elements are x / 2^exponent rounded to nearest even and saturated to
+ * +-448. Head dimension d = 128 only.
+ *
+ * fa_fwd_mx8 computes O = softmax(softmax_scale Q K^T) V and L as fa_fwd does,
+ * with Q, K and V the dequantised block-scaled operands:
+ *   q, k  : (B, Nq or Nk, H, d) E4M3 bytes, densely packed, 16-byte aligned
+ *   qe, ke: (B, Nq or Nk, H, d/32) E8M0 bytes (blocks along d), 4-byte aligned
+ *   vt    : V transposed, (B, H, d, Np) E4M3 bytes, Np = fa_mx8_tokens_padded(Nk)
+ *           (tokens padded with zeros to a multiple of 64)
+ *   vte   : (B, H, Np/32, d) E8M0 bytes: for each block of 32 tokens, the d
+ *           exponents of its rows of V^T
+ *   o     : (B, Nq, H, d) bfloat16, written; lse: (B, H, Nq) float32, written
+ *   softmax_scale: any finite value; causal: 0 or 1 (1 needs Nq == Nk).
+ * Inside, P (at most 2^8 after the running offset) is rounded to E4M3 with a
+ * scale of 1 before P V; row sums stay fp32.
+ * Errors: d != 128 or sizes beyond the kernel's 32-bit tile offsets
+ * (Nk * H * d > 2^30) are FA_ERR_UNSUPPORTED; otherwise as fa_fwd.
+ */
+fa_status fa_fwd_mx8(const uint8_t* q, const uint8_t* qe, const uint8_t* k, const uint8_t* ke,
+                     const uint8_t* vt, const uint8_t* vte, void* o, float* lse, int32_t B,
+                     int32_t Nq, int32_t Nk, int32_t H, int32_t d, float softmax_scale,
+                     int32_t causal, void* stream);
+
+/* Np, the padded token count of vt for N tokens (N rounded up to a multiple of
+ * 64); -1 for N < 0 or too large. */
+int32_t fa_mx8_tokens_padded(int32_t N);
+
+/* Q or K (rows x d, 16-bit of dtype, densely packed, e.g. (B, N, H, d) with
+ * rows = B N H) to the MX format above: xq (rows x d) E4M3 bytes and xe
+ * (rows x d/32) E8M0 bytes, blocks along d. d must be 128. */
+fa_status fa_mx8_quantize_qk(const void* x, int32_t dtype, int64_t rows, int32_t d, uint8_t* xq,
+                             uint8_t* xe, void* stream);
+
+/* V (B, N, H, d) 16-bit of dtype, densely packed, to vt (B, H, d, Np) and vte
+ * (B, H, Np/32, d), blocks of 32 tokens, padding tokens zero. d must be 128. */
+fa_status fa_mx8_quantize_v(const void* v, int32_t dtype, int32_t B, int32_t N, int32_t H,
+                            int32_t d, uint8_t* vt, uint8_t* vte, void* stream);
+
 /* Bytes of the scratch array fa_decode_noalloc holds on each GPU. */
 #define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 

@@ -25,6 +25,9 @@ Readings where the pages are silent (they name FP8 and block scaling only):
     gets -127). Elements are x / 2^e rounded to nearest-even on the E4M3 grid
     and saturated to +-448 (the quotient of the block maximum lies in
     [256, 512), so values above 448 are clamped rather than lost).
+  * A block holding an infinity or a NaN has no finite scale: as in the OCP
+    MX format, its exponent byte is the NaN code 0xFF (exponent 128 here) and
+    its elements are stored as 0; it dequantises to NaN.
   * Q and K are blocked along the head dimension d (the contraction of
     Q K^T), V along the tokens (the contraction of P V), so V is held
     transposed, (d, tokens), with its token count padded with zeros to a
@@ -47,6 +50,7 @@ E4M3_SUBNORMAL_STEP = 2.0 ** -9
 E4M3_EMAX = 8             # exponent of the largest power of two in E4M3
 MX_BLOCK = 32             # elements per shared scale
 E8M0_MIN, E8M0_MAX = -127, 127
+E8M0_NAN = 128            # exponent of the NaN scale byte 0xFF
 V_TOKEN_PAD = 64          # token padding of the transposed V
 
 
@@ -84,12 +88,15 @@ def e4m3_grid() -> np.ndarray:
 
 
 def mx_exponent(amax) -> np.ndarray:
-    """Shared E8M0 exponent of blocks with the given absolute maxima."""
+    """Shared E8M0 exponent of blocks with the given absolute maxima (NaN or
+    infinite maxima give the NaN scale's exponent 128)."""
     amax = np.asarray(amax, dtype=np.float64)
-    with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX
+    finite = np.isfinite(amax)
+    safe = np.where(finite & (amax > 0), amax, 1.0)
+    e = np.floor(np.log2(safe)) - E4M3_EMAX
     e = np.where(amax > 0, e, E8M0_MIN)
-    return np.clip(e, E8M0_MIN, E8M0_MAX).astype(np.int64)
+    e = np.clip(e, E8M0_MIN, E8M0_MAX)
+    return np.where(finite, e, E8M0_NAN).astype(np.int64)
 
 
 def mx_quantize(x, axis: int = -1):
@@ -102,8 +109,12 @@ def mx_quantize(x, axis: int = -1):
     if n % MX_BLOCK:
         raise ValueError("the blocked axis must be a multiple of 32 long")
     blocks = xm.reshape(*xm.shape[:-1], n // MX_BLOCK, MX_BLOCK)
-    e = mx_exponent(np.max(np.abs(blocks), axis=-1))
-    q = e4m3_round(blocks / np.ldexp(1.0, e)[..., None])
+    bad = ~np.all(np.isfinite(blocks), axis=-1)
+    amax = np.where(bad, np.inf, np.max(np.abs(np.where(np.isfinite(blocks), blocks, 0.0)), axis=-1))
+    e = mx_exponent(amax)
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = e4m3_round(blocks / np.ldexp(1.0, np.where(bad, 0, e))[..., None])
+    q = np.where(bad[..., None], 0.0, q)
     return (np.moveaxis(q.reshape(xm.shape), -1, axis),
             np.moveaxis(e, -1, axis))
 
@@ -111,8 +122,9 @@ def mx_quantize(x, axis: int = -1):
 def mx_dequantize(q, e, axis: int = -1) -> np.ndarray:
     """Inverse of mx_quantize's layout: q * 2^e with each exponent over its 32 elements."""
     q = np.asarray(q, dtype=np.float64)
-    scale = np.repeat(np.ldexp(1.0, np.asarray(e)), MX_BLOCK, axis=axis)
-    return q * scale
+    e = np.asarray(e)
+    scale = np.where(e == E8M0_NAN, np.nan, np.ldexp(1.0, np.where(e == E8M0_NAN, 0, e)))
+    return q * np.repeat(scale, MX_BLOCK, axis=axis)
 
 
 def quantize_qk(x):

@@ -173,7 +173,23 @@ def pin_zero_block_and_error_bound(quant):
     assert np.all(np.abs(back - y)[~normal] <= 2.0 ** -10 * X[~normal] + 1e-300)
 
 
-MX_PINS = [pin_block_exponent, pin_power_of_two_exactness, pin_blocks_independent_and_axis,
+def pin_non_finite_block(quant):
+    """A block with an infinity or a NaN gets the NaN scale (exponent 128) and
+    zero elements; its neighbours are untouched."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((3, 64))
+    x[0, 3] = np.inf
+    x[1, 40] = np.nan
+    x[2, 0] = -np.inf
+    q, e = quant(x, -1)
+    assert e[0, 0] == 128 and e[1, 1] == 128 and e[2, 0] == 128
+    assert np.all(q[0, :32] == 0) and np.all(q[1, 32:] == 0) and np.all(q[2, :32] == 0)
+    qr, er = quant(x[:, 32:].copy(), -1)
+    np.testing.assert_array_equal(q[[0, 2], 32:], qr[[0, 2]])
+    assert np.all(np.isnan(F.mx_dequantize(q, e, -1)[0, :32]))
+
+
+MX_PINS = [pin_non_finite_block, pin_block_exponent, pin_power_of_two_exactness, pin_blocks_independent_and_axis,
            pin_zero_block_and_error_bound]
 
 
