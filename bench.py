@@ -41,6 +41,8 @@ PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 PEAK_SCLK_MHZ = 2400.0             # the shader clock that peak is quoted at
 KERNEL_SOURCES = [os.path.join(ROOT, "aware_attention_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_api.hip")]
+KERNEL_SOURCES_MX8 = [os.path.join(ROOT, "aware_attention_amd", "csrc", f)
+                      for f in ("fa_mx8_kernel.hpp", "fa_mx8_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
 
 
@@ -161,15 +163,15 @@ def host_cores() -> dict:
     return info
 
 
-def kernel_digest() -> str:
+def kernel_digest(fp8: bool = False) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES_MX8 if fp8 else KERNEL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, fp8: bool = False):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
     path = TRAFFIC_FILE.format(workload=workload)
     if not os.path.exists(path):
@@ -180,7 +182,7 @@ def read_traffic(workload: str):
             if "=" in line and not line.startswith("#"):
                 a, b = line.split("=", 1)
                 kv[a.strip()] = b.strip()
-    if kv.get("kernel_digest") != kernel_digest():
+    if kv.get("kernel_digest") != kernel_digest(fp8):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -473,7 +475,8 @@ def main():
     assert not torch.isnan(lse).any() and not torch.isposinf(lse).any(), \
         "NaN or +inf log-sum-exp in the timed output"
 
-    traffic = read_traffic(args.workload + ("_bwd" if args.backward else ""))
+    traffic = read_traffic(args.workload + ("_bwd" if args.backward else "")
+                           + ("_fp8" if args.fp8 else ""), args.fp8)
     if decode:
         gbs = spec.bytes_compulsory() / (ms_per_step * 1e-3) / 1e9
         out = {
@@ -512,9 +515,9 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": None if fp8 else traffic,
+            "traffic": traffic,
         },
-        "kernel_digest": kernel_digest(),
+        "kernel_digest": kernel_digest(fp8),
         "wall_s_timed": round(wall, 4),
         "warmup_launches": warm_launches,
         "warmup_s": round(warm_s, 3),
