@@ -18,6 +18,9 @@
 //     (Q and dO rows in VGPRs, L and D lane-local); 64-key tiles of K and V
 //     stream through LDS. Per tile: S^T = K Q^T and dP^T = V dO^T, dS^T in
 //     registers, then dQ^T += K^T dS^T (A operand: transposing reads of K).
+//     Its state fits 256 registers at every d, so two workgroups share a CU
+//     (two waves per SIMD: one wave's exponentials overlap the other's
+//     products); the dK/dV kernel does the same where it fits (kDkdvWaves).
 // dQ is produced by its own pass over the keys (S and dP recomputed once more)
 // instead of by atomic adds, so the library needs no accumulation buffer.
 //
@@ -78,6 +81,13 @@ constexpr int kBwdRows = 32 * kBwdWaves;   // rows a workgroup owns
 constexpr int kBwdTile = 64;               // rows of a streamed LDS tile
 constexpr int kReadAhead = 4;              // LDS operand reads in flight ahead of the products (dQ)
 constexpr float kLog2eF = 1.44269504088896340736f;
+// Waves per SIMD of the dK/dV kernel: two workgroups share a CU (two waves
+// per SIMD, so one wave's exponentials overlap the other's products) where
+// the per-lane state fits in 256 registers without spilling: d = 32, and
+// d = 64 except the local pattern. At d = 128 one wave holds its K, V rows
+// and both accumulators in up to 512 registers.
+template <int D, bool LOCAL>
+constexpr int kDkdvWaves = (D == 32 || (D == 64 && !LOCAL)) ? 2 : 1;
 
 template <bool F16>
 __device__ __forceinline__ float half_to_float(uint16_t b) {
@@ -300,7 +310,7 @@ __device__ __forceinline__ KpmSpan kpm_span(const uint8_t* row, int n, int* red,
 template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false,
           bool LOCAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(kDkdvWaves<D, LOCAL>, kDkdvWaves<D, LOCAL>)))
 void dkdv_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
@@ -550,7 +560,7 @@ void dkdv_kernel(BwdParams p) {
 template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false,
           bool LOCAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
