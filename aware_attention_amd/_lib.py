@@ -7,7 +7,11 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# The library: libfa.so next to this file, or the build that the environment
+# variable AWARE_ATTENTION_LIB names (the timing-perturbed libfa_stress.so of
+# the race tests). Either way it must exist: there is no fallback.
+LIB_PATH = os.environ.get("AWARE_ATTENTION_LIB") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK = 0
 FA_ERR_INVALID_ARGUMENT = 1

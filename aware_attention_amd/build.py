@@ -13,6 +13,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
+# The timing-perturbed library for the race tests (-DFA_STRESS: pseudo-random
+# pauses where waves hand LDS buffers to one another); loaded only when the
+# environment variable AWARE_ATTENTION_LIB names it.
+LIB_STRESS = os.path.join(PKG, "libfa_stress.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -39,9 +43,11 @@ def _messages(res) -> list[str]:
     return [ln for ln in (res.stdout + res.stderr).splitlines() if _NOISE not in ln]
 
 
-def build(verbose: bool = True) -> str:
-    objs = [os.path.join(CSRC, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [hipcc_compile(s, o) for s, o in zip(SOURCES, objs)]
+def build(verbose: bool = True, stress: bool = False) -> str:
+    suffix = "_stress" if stress else ""
+    objs = [os.path.join(CSRC, os.path.splitext(s)[0] + suffix + ".o") for s in SOURCES]
+    extra = ["-DFA_STRESS"] if stress else []
+    cmds = [hipcc_compile(s, o, extra) for s, o in zip(SOURCES, objs)]
     procs = []
     for cmd in cmds:
         if verbose:
@@ -59,19 +65,20 @@ def build(verbose: bool = True) -> str:
             print("\n".join(msgs), flush=True)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
-    tmp = LIB + ".tmp"
+    lib = LIB_STRESS if stress else LIB
+    tmp = lib + ".tmp"
     link = [HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp]
     if verbose:
         print("[build]", " ".join(link), flush=True)
     res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc link failed:\n" + "\n".join(_messages(res)))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     for o in objs:
         os.remove(o)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(stress="--stress" in sys.argv[1:])
     sys.exit(0)

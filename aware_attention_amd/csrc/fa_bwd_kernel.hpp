@@ -548,6 +548,7 @@ void dkdv_kernel(BwdParams p) {
     }
     }
     if (more && tid < kBwdTile) store_ld(buf ^ 1, qt_next, nx);
+    stress_pause(it);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }
@@ -781,6 +782,7 @@ void dq_kernel(BwdParams p) {
       }
     }
     }
+    stress_pause(it);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }

@@ -241,6 +241,7 @@ void fwd256_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0x7);   // only ALU work may cross
       }
     }
+    stress_pause(kt);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }

@@ -169,6 +169,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Timing-perturbed build (compiled with -DFA_STRESS into a library of its own
+// for the race tests): a wave-uniform pseudo-random pause of 0..7 x 64 cycles
+// at the points where waves hand LDS buffers to one another, so that a
+// missing wait or barrier shows as a wrong result instead of staying hidden
+// by the usual timing. Compiles to nothing otherwise.
+__device__ __forceinline__ void stress_pause(int salt) {
+#ifdef FA_STRESS
+  uint32_t h = ((uint32_t)blockIdx.x * 0x9E3779B1u) ^ ((uint32_t)(threadIdx.x >> 6) * 0x85EBCA77u) ^
+               ((uint32_t)salt * 0xC2B2AE3Du);
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  const int n = __builtin_amdgcn_readfirstlane((int)(h & 7u));
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
+#else
+  (void)salt;
+#endif
+}
+
 // Workgroup barrier without a memory fence: LDS operand reads of the current
 // tiles may stay in flight across it (they are read-only). The copies into
 // LDS are made visible explicitly (s_waitcnt by the issuing waves before the
@@ -767,18 +786,23 @@ void fwd_kernel(FwdParams p) {
     }
   }
   auto period = [&](int j) __attribute__((always_inline)) {
+    stress_pause(4 * j);
     if (!group_b) {
       if (j < kt_end) {
         if (j + 1 < kt_end) copy_k(j + 1);
         copy_v(j);
       }
       mfma_phase(j);
+      stress_pause(4 * j + 1);
       if (j < kt_end && active(j)) softmax(j);
+      stress_pause(4 * j + 2);
       __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
     } else {
       if (j > kt0 && active(j - 1)) softmax(j - 1);
+      stress_pause(4 * j + 1);
       mfma_phase(j);
     }
+    stress_pause(4 * j + 3);
     barrier_nofence();
   };
   if (kt0 < kt_end) {   // a band can leave a workgroup without any key
@@ -787,6 +811,7 @@ void fwd_kernel(FwdParams p) {
     __syncthreads();
     for (int j = kt0; j < js0; ++j) period(j);
     for (int j = js0; j < js1; ++j) {
+      stress_pause(4 * j);
       if (!group_b) {
         const uint8_t* gk = kg + (int64_t)((j + 1) * BC) * k_tb;
         const uint8_t* gv = vg + (int64_t)(j * BC) * v_tb;
@@ -798,12 +823,16 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
         });
+        stress_pause(4 * j + 1);
         softmax_tile(std::false_type{}, 0, 0u);
+        stress_pause(4 * j + 2);
         __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
       } else {
         softmax_tile(std::false_type{}, 0, 0u);
+        stress_pause(4 * j + 1);
         qk_pv(j, [] {});
       }
+      stress_pause(4 * j + 3);
       barrier_nofence();
     }
     for (int j = js1; j <= kt_end; ++j) period(j);

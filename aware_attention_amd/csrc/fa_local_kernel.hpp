@@ -189,6 +189,7 @@ void fwd_local_kernel(LocalParams p) {
   // ahead of that wait.
   auto publish = [&](int newer) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
+    stress_pause(newer);
     wait_tile<D, R>(newer);
     barrier_nofence();
   };

@@ -386,18 +386,23 @@ void fwd_mx8_kernel(Mx8Params p) {
   auto period = [&](int j) __attribute__((always_inline)) {
     const bool do_qk = j < n_kt && active(j);
     const bool do_pv = j > 0 && active(j - 1);
+    stress_pause(4 * j);
     if (!group_b) {
       if (j < n_kt) {
         if (j + 1 < n_kt) copy_k(j + 1);
         copy_v(j);
       }
       mfma_phase(do_qk, do_pv, j);
+      stress_pause(4 * j + 1);
       if (j < n_kt && active(j)) softmax(j);
+      stress_pause(4 * j + 2);
       __builtin_amdgcn_s_waitcnt(0);
     } else {
       if (j > 0 && active(j - 1)) softmax(j - 1);
+      stress_pause(4 * j + 1);
       mfma_phase(do_qk, do_pv, j);
     }
+    stress_pause(4 * j + 3);
     barrier_nofence();
   };
   const int full_kt = Nk / BC;
@@ -409,16 +414,21 @@ void fwd_mx8_kernel(Mx8Params p) {
   __syncthreads();
   for (int j = 0; j < js0; ++j) period(j);
   for (int j = js0; j < js1; ++j) {   // steady: full, unmasked, active tiles for every wave
+    stress_pause(4 * j);
     if (!group_b) {
       copy_k(j + 1);
       copy_v(j);
       qk_pv(std::true_type{}, std::true_type{}, j);
+      stress_pause(4 * j + 1);
       softmax_tile(std::false_type{}, 0);
+      stress_pause(4 * j + 2);
       __builtin_amdgcn_s_waitcnt(0);
     } else {
       softmax_tile(std::false_type{}, 0);
+      stress_pause(4 * j + 1);
       qk_pv(std::true_type{}, std::true_type{}, j);
     }
+    stress_pause(4 * j + 3);
     barrier_nofence();
   }
   for (int j = js1; j <= n_kt; ++j) period(j);
