@@ -22,10 +22,16 @@ library is missing or the device is not a gfx950, calls raise.
     fa_fwd_varlen_strided with no copy.
     dq, dk, dv, delta = fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False)
     dq, dk, dv, delta = fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, ...)
-        the backward (contiguous tensors of one half-precision type): S and P are
-        recomputed from lse; delta = rowsum(dout * o), laid out like lse.
+        the backward (tensors of one half-precision type): S and P are recomputed
+        from lse; delta = rowsum(dout * o), laid out like lse. The tensors (dq, dk
+        and dv passed in too) may be strided views under the forward's rules
+        (fa_bwd_strided / fa_bwd_varlen_strided, no copy).
     o = attention(q, k, v, softmax_scale=None, causal=False)
         forward with autograd: o.backward(...) runs fa_bwd.
+    o = attention_qkvpacked(qkv, softmax_scale=None, causal=False)
+        the same from one packed (B, S, 3, H, d) (or, with cu_seqlens, (total, 3,
+        H, d)) tensor: both passes read its three views in place and the
+        gradient is one packed tensor that the backward's kernels write.
     o, lse = fa_decode(q, k, v, seqlens_k=None, softmax_scale=None)
         one query per (batch, head), q (B,1,H,d), k/v (B,Nk,H,d) the cache, split
         over the cache and merged through the log-sum-exps (fa_decode).
@@ -48,14 +54,15 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_ERR_HIP, FA_ERR_INVALID_ARGUMENT,
                    FA_ERR_UNSUPPORTED, FA_OK, FaError, check, decode_workspace_bytes, load,
                    raw_fa_bwd, raw_fa_bwd_band, raw_fa_bwd_padded, raw_fa_bwd_varlen,
-                   raw_fa_bwd_local, raw_fa_bwd_varlen_band, raw_fa_decode, raw_fa_fwd_local,
+                   raw_fa_bwd_local, raw_fa_bwd_varlen_band, raw_fa_bwd_strided,
+                   raw_fa_bwd_varlen_strided, raw_fa_decode, raw_fa_fwd_local,
                    raw_fa_fwd, raw_fa_fwd_band, raw_fa_fwd_padded, raw_fa_fwd_strided,
                    raw_fa_fwd_varlen,
                    raw_fa_fwd_varlen_band, raw_fa_fwd_varlen_strided, raw_fa_fwd_mx8,
                    raw_fa_mx8_quantize_qk, raw_fa_mx8_quantize_v, mx8_tokens_padded)
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_fwd_local", "fa_bwd", "fa_bwd_varlen", "fa_decode",
-           "attention", "mx8_quantize_qk", "mx8_quantize_v", "fa_fwd_mx8", "attention_mx8",
+           "attention", "attention_qkvpacked", "mx8_quantize_qk", "mx8_quantize_v", "fa_fwd_mx8", "attention_mx8",
            "FaError", "load",
            "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
 
@@ -252,12 +259,20 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=Fa
     return out, lse
 
 
-def _check_contiguous(ts, names, dtype):
+def _check_dtypes(ts, names, dtype):
     for t, n in zip(ts, names):
-        if not t.is_contiguous():
-            raise ValueError(f"{n} must be contiguous for the backward")
         if t.dtype != dtype:
             raise TypeError(f"{n} must be {dtype} like q (got {t.dtype})")
+
+
+def _grad_out(g, like, q, name):
+    """A gradient output: allocated like `like` (contiguous), or the caller's
+    tensor of that shape and q's dtype, on q's device (any strides)."""
+    torch = _torch()
+    if g is None:
+        return torch.empty(like.shape, dtype=like.dtype, device=like.device)
+    _check_tensor(g, name, like.dim())
+    return _check_aux(g, name, q, like.shape, q.dtype, contiguous=False, dtype_error=TypeError)
 
 
 def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None,
@@ -274,18 +289,24 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=
             or o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("shape mismatch among q, k, v, o and dout")
     _same_device(q, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"))
-    _check_contiguous((q, k, v, o, dout), ("q", "k", "v", "o", "dout"), q.dtype)
-    dq, dk, dv = (torch.empty_like(x) if g is None else
-                  _check_aux(g, n, q, x.shape, q.dtype, dtype_error=TypeError)
-                  for g, x, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")))
+    _check_dtypes((k, v, o, dout), ("k", "v", "o", "dout"), q.dtype)
+    dq, dk, dv = (_grad_out(g, x, q, n) for g, x, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")))
     _check_aux(lse, "lse", q, (B, H, Nq), torch.float32)
     delta = _lse(delta, q, (B, H, Nq), "delta")
+    ts = (q, k, v, o, dout, dq, dk, dv)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
     dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
+    strided = not all(t.is_contiguous() for t in ts)
+    if strided and (local is not None or key_padding_mask is not None):
+        raise ValueError("the backward with local or key_padding_mask needs contiguous tensors")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if local is not None:
+        if strided:
+            wl, wr = (-1, -1) if window is None else _window(window, causal)
+            check(raw_fa_bwd_strided(*ptrs, B, Nq, Nk, H, d, [x for t in ts for x in _strides(t)],
+                                     dt, scale, int(bool(causal)), wl, wr, stream))
+        elif local is not None:
             if window is not None or key_padding_mask is not None or Nk != Nq:
                 raise ValueError("local: self-attention only, without a window or padding mask")
             clamp = lambda x: max(min(int(x), 2**31 - 1), -1)  # noqa: E731
@@ -323,18 +344,22 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=N
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
             or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
-    _check_contiguous((q, k, v, o, dout), ("q", "k", "v", "o", "dout"), q.dtype)
-    dq, dk, dv = (torch.empty_like(q) if g is None else
-                  _check_aux(g, n, q, q.shape, q.dtype, dtype_error=TypeError)
-                  for g, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    _check_dtypes((k, v, o, dout), ("k", "v", "o", "dout"), q.dtype)
+    dq, dk, dv = (_grad_out(g, q, q, n) for g, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
     _check_aux(lse, "lse", q, (H, total), torch.float32)
     delta = _lse(delta, q, (H, total), "delta")
+    ts = (q, k, v, o, dout, dq, dk, dv)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens.data_ptr())
     dt, scale = _dtype_code(q.dtype), _scale(softmax_scale, d)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if window is not None:
+        if not all(t.is_contiguous() for t in ts):
+            wl, wr = (-1, -1) if window is None else _window(window, causal)
+            check(raw_fa_bwd_varlen_strided(*ptrs, cu_seqlens.numel() - 1, int(max_seqlen), total,
+                                            H, d, [x for t in ts for x in _strides(t)], dt, scale,
+                                            int(bool(causal)), wl, wr, stream))
+        elif window is not None:
             wl, wr = _window(window, causal)
             check(raw_fa_bwd_varlen_band(*ptrs, cu_seqlens.numel() - 1, int(max_seqlen), total, H,
                                          d, dt, scale, wl, wr, stream))
@@ -350,7 +375,10 @@ def _autograd_function():
     class _Attention(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q, k, v, softmax_scale, causal, window, key_padding_mask, local):
-            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            if local is not None or key_padding_mask is not None:
+                q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            else:   # views the kernels read in place are kept
+                q, k, v = _kernel_view(q), _kernel_view(k), _kernel_view(v)
             if local is not None:
                 if window is not None or key_padding_mask is not None:
                     raise ValueError("local excludes window and key_padding_mask")
@@ -368,7 +396,9 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, dout):
             q, k, v, o, lse = ctx.saved_tensors
-            dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, dout.contiguous(),
+            plain = ctx.local is None and ctx.key_padding_mask is None
+            dout = _kernel_view(dout) if plain else dout.contiguous()
+            dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, dout,
                                    softmax_scale=ctx.softmax_scale, causal=ctx.causal,
                                    window=ctx.window, key_padding_mask=ctx.key_padding_mask,
                                    local=ctx.local)
@@ -377,7 +407,78 @@ def _autograd_function():
     return _Attention
 
 
+def _kernel_view(t, token_dim=-3):
+    """t itself when the strided entry points can read it in place (contiguous
+    last dimension, other strides multiples of 8 elements, token stride at most
+    2^24), else a contiguous copy."""
+    if t.stride(-1) == 1 and all(x >= 0 and x % 8 == 0 for x in _strides(t)) \
+            and (t.shape[token_dim] <= 1 or t.stride(token_dim) <= 2**24):
+        return t
+    return t.contiguous()
+
+
+def _qkvpacked_function():
+    torch = _torch()
+
+    class _QKVPacked(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, qkv, softmax_scale, causal, window, cu_seqlens, max_seqlen):
+            qkv = _kernel_view(qkv, token_dim=-4)
+            q, k, v = qkv.unbind(-3)
+            if cu_seqlens is None:
+                o, lse = fa_fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window=window)
+            else:
+                o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen,
+                                       softmax_scale=softmax_scale, causal=causal, window=window)
+            ctx.save_for_backward(qkv, o, lse, cu_seqlens)
+            ctx.args = (softmax_scale, causal, window, max_seqlen)
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            qkv, o, lse, cu_seqlens = ctx.saved_tensors
+            softmax_scale, causal, window, max_seqlen = ctx.args
+            q, k, v = qkv.unbind(-3)
+            dqkv = torch.empty(qkv.shape, dtype=qkv.dtype, device=qkv.device)
+            dq, dk, dv = dqkv.unbind(-3)
+            dout = _kernel_view(dout)
+            if cu_seqlens is None:
+                fa_bwd(q, k, v, o, lse, dout, softmax_scale=softmax_scale, causal=causal,
+                       dq=dq, dk=dk, dv=dv, window=window)
+            else:
+                fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen,
+                              softmax_scale=softmax_scale, causal=causal, dq=dq, dk=dk, dv=dv,
+                              window=window)
+            return dqkv, None, None, None, None, None
+
+    return _QKVPacked
+
+
 _ATTENTION_FN = None
+_QKVPACKED_FN = None
+
+
+def attention_qkvpacked(qkv, softmax_scale=None, causal=False, window=None, cu_seqlens=None,
+                        max_seqlen=None):
+    """o = softmax(scale q k^T) v with q, k, v the three views of one packed tensor,
+    differentiable: qkv (B, S, 3, H, d) -> o (B, S, H, d), or with cu_seqlens
+    (int32 (num_seqs + 1,)) and max_seqlen, qkv (total, 3, H, d) -> o (total, H, d).
+    The forward (fa_fwd_strided / fa_fwd_varlen_strided) and the backward
+    (fa_bwd_strided / fa_bwd_varlen_strided) read the views in place; the
+    backward writes dq, dk and dv into the views of one packed gradient, so no
+    copy is made either way (the packed layout of the unmasked path in
+    "InternViT-6B-448px-V1-2 如何加速注意力计算", section
+    FlashAttention 封装类三条执行路径)."""
+    global _QKVPACKED_FN
+    want = 5 if cu_seqlens is None else 4
+    if getattr(qkv, "dim", lambda: -1)() != want or qkv.shape[-3] != 3:
+        raise ValueError(f"qkv must be a {'(B, S, 3, H, d)' if want == 5 else '(total, 3, H, d)'} "
+                         f"tensor (got shape {tuple(getattr(qkv, 'shape', ()))})")
+    if cu_seqlens is not None and max_seqlen is None:
+        raise ValueError("max_seqlen is required with cu_seqlens")
+    if _QKVPACKED_FN is None:
+        _QKVPACKED_FN = _qkvpacked_function()
+    return _QKVPACKED_FN.apply(qkv, softmax_scale, causal, window, cu_seqlens, max_seqlen)
 
 
 def attention(q, k, v, softmax_scale=None, causal=False, window=None, key_padding_mask=None,

@@ -23,7 +23,8 @@ FA_DTYPE_F16 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_band", "fa_fwd_varlen_band", "fa_fwd_strided",
             "fa_fwd_varlen_strided", "fa_fwd_padded", "fa_bwd", "fa_bwd_varlen", "fa_bwd_band",
-            "fa_bwd_varlen_band", "fa_bwd_padded", "fa_decode", "fa_fwd_local", "fa_bwd_local",
+            "fa_bwd_varlen_band", "fa_bwd_padded", "fa_bwd_strided", "fa_bwd_varlen_strided",
+            "fa_decode", "fa_fwd_local", "fa_bwd_local",
             "fa_decode_workspace_bytes", "fa_decode_noalloc", "fa_fwd_mx8",
             "fa_mx8_tokens_padded", "fa_mx8_quantize_qk", "fa_mx8_quantize_v", "fa_status_string",
             "fa_last_error", "fa_abi_version")
@@ -73,6 +74,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_varlen_band.restype = i32
     lib.fa_bwd_padded.argtypes = [vp] * 11 + [i32] * 5 + [f32, i32, vp]
     lib.fa_bwd_padded.restype = i32
+    lib.fa_bwd_strided.argtypes = [vp] * 10 + [i32] * 5 + [p64, i32, f32, i32, i32, i32, vp]
+    lib.fa_bwd_strided.restype = i32
+    lib.fa_bwd_varlen_strided.argtypes = [vp] * 11 + [i32] * 5 + [p64, i32, f32, i32, i32, i32, vp]
+    lib.fa_bwd_varlen_strided.restype = i32
     lib.fa_fwd_local.argtypes = [vp] * 5 + [i32] * 5 + [f32] + [i32] * 5 + [vp]
     lib.fa_fwd_local.restype = i32
     lib.fa_bwd_local.argtypes = [vp] * 10 + [i32] * 5 + [f32] + [i32] * 5 + [vp]
@@ -160,6 +165,25 @@ def raw_fa_fwd_varlen_strided(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, 
     return load().fa_fwd_varlen_strided(q, k, v, o, lse, cu, num_seqs, max_seqlen, total, H, d,
                                         _int64_array(q_strides), _int64_array(k_strides),
                                         _int64_array(v_strides), _int64_array(o_strides), dtype,
+                                        scale, causal, window_left, window_right, stream)
+
+
+def raw_fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, strides, dtype,
+                       scale, causal, window_left, window_right, stream) -> int:
+    """Pointer-level call of fa_bwd_strided (strides: 24 ints, the (batch, token, head)
+    strides of q, k, v, o, dout, dq, dk, dv); returns the status code."""
+    return load().fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d,
+                                 _int64_array(strides), dtype, scale, causal, window_left,
+                                 window_right, stream)
+
+
+def raw_fa_bwd_varlen_strided(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs, max_seqlen,
+                              total, H, d, strides, dtype, scale, causal, window_left,
+                              window_right, stream) -> int:
+    """Pointer-level call of fa_bwd_varlen_strided (strides: 16 ints, the (token, head)
+    strides of q, k, v, o, dout, dq, dk, dv); returns the status code."""
+    return load().fa_bwd_varlen_strided(q, k, v, o, dout, lse, dq, dk, dv, delta, cu, num_seqs,
+                                        max_seqlen, total, H, d, _int64_array(strides), dtype,
                                         scale, causal, window_left, window_right, stream)
 
 

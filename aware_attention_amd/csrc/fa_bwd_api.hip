@@ -1,6 +1,7 @@
-// C ABI of the backward pass (fa_bwd, fa_bwd_varlen, and their band,
-// padding-mask and local-window forms): argument checks and the three
-// launches. The operation is documented in include/fa.h.
+// C ABI of the backward pass (fa_bwd, fa_bwd_varlen, their band,
+// padding-mask and local-window forms, and the strided forms fa_bwd_strided
+// and fa_bwd_varlen_strided): argument checks and the three launches. The
+// operation is documented in include/fa.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,8 +22,11 @@ using fa_host::fail;
 template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND, bool KPM, bool LOCAL>
 hipError_t launch_bwd_t(const fa::BwdParams& p, int64_t nrows, int N, uint32_t grid_k,
                         uint32_t grid_q, hipStream_t stream) {
-  hipLaunchKernelGGL((fa::delta_kernel<D, F16>), dim3((uint32_t)((nrows + 255) / 256)), dim3(256),
-                     0, stream, p.o, p.dout, p.delta, nrows, p.H, N);
+  constexpr int kDeltaRows = fa::kDeltaThreads / (D / 8);
+  hipLaunchKernelGGL((fa::delta_kernel<D, F16>),
+                     dim3((uint32_t)((nrows + kDeltaRows - 1) / kDeltaRows)),
+                     dim3(fa::kDeltaThreads), 0, stream, p.o, p.dout, p.delta, p.H, N, (int)nrows,
+                     p.st[fa::kTO], p.st[fa::kTdO]);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>), dim3(grid_k),
@@ -107,8 +111,6 @@ constexpr int64_t kMaxBandLenBwd = int64_t{1} << 29;
 
 fa_status check_bwd_common(int32_t H, int32_t d, int32_t dtype, float scale, int32_t causal) {
   if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1");
-  // The tile copies address a 64-row tile with 32-bit byte offsets.
-  if ((int64_t)H * d > (int64_t{1} << 24)) return fail(FA_ERR_UNSUPPORTED, "H * d above 2^24");
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
@@ -125,6 +127,46 @@ bool all_aligned(const void* const* ptrs, int n) {
 
 constexpr float kLog2eHost = 1.44269504088896340736f;
 
+using Strides = fa::BwdStrides;
+const char* const kBwdNames[fa::kBwdTensors] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
+// Token strides up to 2^24 elements keep the per-lane 32-bit byte offsets of
+// the kernels' 64-row tile copies in range.
+constexpr int64_t kMaxTokenStrideBwd = int64_t{1} << 24;
+
+fa_status check_bwd_strides(const Strides st[fa::kBwdTensors]) {
+  for (int i = 0; i < fa::kBwdTensors; ++i) {
+    const Strides& s = st[i];
+    const std::string name = kBwdNames[i];
+    if (s.b < 0 || s.t < 0 || s.h < 0) return fail(FA_ERR_INVALID_ARGUMENT, name + ": strides must be >= 0");
+    if ((s.b | s.t | s.h) & 7)
+      return fail(FA_ERR_INVALID_ARGUMENT,
+                  name + ": strides must be multiples of 8 elements (16-byte aligned rows)");
+    if (s.t > kMaxTokenStrideBwd)
+      return fail(FA_ERR_UNSUPPORTED, name + ": token stride above 2^24 elements");
+  }
+  return FA_OK;
+}
+
+// Densely packed (B, Nq|Nk, H, d) tensors (varlen: (total, H, d), the batch
+// strides unused).
+void contiguous_bwd(int64_t Nq, int64_t Nk, int32_t H, int32_t d, Strides st[fa::kBwdTensors]) {
+  const int64_t t = (int64_t)H * d;
+  const Strides sq{Nq * t, t, d}, sk{Nk * t, t, d};
+  st[fa::kTQ] = st[fa::kTO] = st[fa::kTdO] = st[fa::kTdQ] = sq;
+  st[fa::kTK] = st[fa::kTV] = st[fa::kTdK] = st[fa::kTdV] = sk;
+}
+
+// Strides from the caller's array: n entries per tensor (3 dense: batch,
+// token, head; 2 varlen: token, head), tensors in the order of BwdTensor.
+fa_status read_bwd_strides(const int64_t* in, int n, Strides st[fa::kBwdTensors]) {
+  if (!in) return fail(FA_ERR_INVALID_ARGUMENT, "null stride array");
+  for (int i = 0; i < fa::kBwdTensors; ++i) {
+    const int64_t* x = in + n * i;
+    st[i] = n == 3 ? Strides{x[0], x[1], x[2]} : Strides{0, x[0], x[1]};
+  }
+  return check_bwd_strides(st);
+}
+
 // Local window + anchors of fa_bwd_local (the forward's fa_fwd_local pattern).
 struct LocalPattern {
   int32_t n_global, map_w, win_rows, win_cols;
@@ -136,7 +178,7 @@ fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, 
                     int32_t Nq, int32_t Nk, int32_t H, int32_t d, int32_t dtype,
                     float softmax_scale, int32_t causal, BwdMask mask, int32_t win_left,
                     int32_t win_right, const uint8_t* kpm, void* stream,
-                    const LocalPattern* loc = nullptr) {
+                    const LocalPattern* loc = nullptr, const Strides* strides = nullptr) {
   const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
   for (const void* x : ptrs)
     if (!x) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -149,12 +191,15 @@ fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, 
   if (loc && Nq > kMaxLocalTokensBwd)
     return fail(FA_ERR_UNSUPPORTED, "local attention supports N <= 2^28");
   if (!all_aligned(ptrs, 10)) return fail(FA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if (!strides && (int64_t)H * d > kMaxTokenStrideBwd)
+    return fail(FA_ERR_UNSUPPORTED, "H * d above 2^24");
   const int64_t units = (int64_t)H * B;
   const int64_t grid_k = (Nk + fa::kBwdRows - 1) / fa::kBwdRows * units;
   const int64_t grid_q = (Nq + fa::kBwdRows - 1) / fa::kBwdRows * units;
   const int64_t nrows = (int64_t)B * Nq * H;
-  if (grid_k > INT32_MAX || grid_q > INT32_MAX || (nrows + 255) / 256 > INT32_MAX)
-    return fail(FA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  // (the D = dO . O launch numbers its rows with 32-bit integers)
+  if (grid_k > INT32_MAX || grid_q > INT32_MAX || nrows > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "too many tiles or rows (B * N * H above 2^31 - 1) for one launch");
   st = check_device();
   if (st != FA_OK) return st;
 
@@ -170,9 +215,10 @@ fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.cu_seqlens = nullptr;
-  p.row_stride = (int64_t)H * d;
-  p.q_batch_stride = (int64_t)Nq * H * d;
-  p.k_batch_stride = (int64_t)Nk * H * d;
+  if (strides)
+    std::copy(strides, strides + fa::kBwdTensors, p.st);
+  else
+    contiguous_bwd(Nq, Nk, H, d, p.st);
   p.lse_batch_stride = (int64_t)H * Nq;
   p.lse_head_stride = Nq;
   p.Nq = Nq;
@@ -208,7 +254,7 @@ fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
                      float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
                      int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
                      float softmax_scale, int32_t causal, BwdMask mask, int32_t win_left,
-                     int32_t win_right, void* stream) {
+                     int32_t win_right, void* stream, const Strides* strides = nullptr) {
   if (!cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
   if (num_seqs < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
   if (total < 0 || max_seqlen < 0) return fail(FA_ERR_INVALID_ARGUMENT, "total and max_seqlen must be >= 0");
@@ -217,6 +263,8 @@ fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
   if (st != FA_OK) return st;
   if (mask == BwdMask::kBand && max_seqlen > kMaxBandLenBwd)
     return fail(FA_ERR_UNSUPPORTED, "banded attention supports max_seqlen <= 2^29");
+  if (!strides && (int64_t)H * d > kMaxTokenStrideBwd)
+    return fail(FA_ERR_UNSUPPORTED, "H * d above 2^24");
   if (total == 0 || max_seqlen == 0) return FA_OK;   // nothing to compute
   const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
   for (const void* x : ptrs)
@@ -227,8 +275,8 @@ fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
   const int64_t n_t = (max_seqlen + fa::kBwdRows - 1) / fa::kBwdRows;
   const int64_t grid = n_t * units;
   const int64_t nrows = (int64_t)total * H;
-  if (grid > INT32_MAX || (nrows + 255) / 256 > INT32_MAX)
-    return fail(FA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  if (grid > INT32_MAX || nrows > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "too many tiles or rows (B * N * H above 2^31 - 1) for one launch");
   st = check_device();
   if (st != FA_OK) return st;
 
@@ -244,9 +292,10 @@ fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.cu_seqlens = cu_seqlens;
-  p.row_stride = (int64_t)H * d;
-  p.q_batch_stride = 0;
-  p.k_batch_stride = 0;
+  if (strides)
+    std::copy(strides, strides + fa::kBwdTensors, p.st);
+  else
+    contiguous_bwd(total, total, H, d, p.st);
   p.lse_batch_stride = 0;
   p.lse_head_stride = total;
   p.Nq = 0;
@@ -268,6 +317,19 @@ fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
 fa_status check_bwd_window(int32_t left, int32_t right) {
   if (left < -1 || right < -1)
     return fail(FA_ERR_INVALID_ARGUMENT, "window sides must be >= 0, or -1 for unbounded");
+  return FA_OK;
+}
+
+// The mask named by a causal flag and a window, as taken by the strided
+// entry points: causal, or no mask when both sides are unbounded, else a band.
+fa_status bwd_mask_of(int32_t causal, int32_t left, int32_t right, BwdMask* mask) {
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  const fa_status st = check_bwd_window(left, right);
+  if (st != FA_OK) return st;
+  const bool unbounded = left == -1 && right == -1;
+  if (causal && !unbounded)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal and a window are exclusive (causal is window (-1, 0))");
+  *mask = causal ? BwdMask::kCausal : (unbounded ? BwdMask::kNone : BwdMask::kBand);
   return FA_OK;
 }
 
@@ -348,6 +410,42 @@ fa_status fa_bwd_local(const void* q, const void* k, const void* v, const void* 
   return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, N, N, H, d, dtype, softmax_scale,
                    causal, causal ? BwdMask::kLocalCausal : BwdMask::kLocal, -1, -1, nullptr,
                    stream, &loc);
+}
+
+fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                         const int64_t* strides, int32_t dtype, float softmax_scale,
+                         int32_t causal, int32_t window_left, int32_t window_right,
+                         void* stream) {
+  fa_host::g_last_error.clear();
+  Strides st[fa::kBwdTensors];
+  fa_status s = read_bwd_strides(strides, 3, st);
+  if (s != FA_OK) return s;
+  BwdMask mask;
+  s = bwd_mask_of(causal, window_left, window_right, &mask);
+  if (s != FA_OK) return s;
+  return dense_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Nq, Nk, H, d, dtype, softmax_scale,
+                   causal, mask, window_left, window_right, nullptr, stream, nullptr, st);
+}
+
+fa_status fa_bwd_varlen_strided(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t max_seqlen, int32_t total, int32_t H, int32_t d,
+                                const int64_t* strides, int32_t dtype, float softmax_scale,
+                                int32_t causal, int32_t window_left, int32_t window_right,
+                                void* stream) {
+  fa_host::g_last_error.clear();
+  Strides st[fa::kBwdTensors];
+  fa_status s = read_bwd_strides(strides, 2, st);
+  if (s != FA_OK) return s;
+  BwdMask mask;
+  s = bwd_mask_of(causal, window_left, window_right, &mask);
+  if (s != FA_OK) return s;
+  return varlen_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, cu_seqlens, num_seqs, max_seqlen,
+                    total, H, d, dtype, softmax_scale, causal, mask, window_left, window_right,
+                    stream, st);
 }
 
 }  // extern "C"

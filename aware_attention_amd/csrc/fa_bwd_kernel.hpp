@@ -36,6 +36,18 @@
 
 namespace fa {
 
+// Tensors of the backward, in the order of BwdParams::st.
+enum BwdTensor { kTQ, kTK, kTV, kTO, kTdO, kTdQ, kTdK, kTdV, kBwdTensors };
+
+// Strides of one tensor in elements (the head dimension is contiguous):
+// batch (dense only), token (the packed row index when varlen), head. Every
+// stride is a multiple of 8 (16-byte aligned rows) and token strides are at
+// most 2^24, which keeps the per-lane 32-bit byte offsets of a 64-row tile in
+// range.
+struct BwdStrides {
+  int64_t b, t, h;
+};
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -48,9 +60,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   const int32_t* cu_seqlens;   // varlen only
-  int64_t row_stride;          // elements between tokens: H * d (all tensors)
-  int64_t q_batch_stride;      // dense: Nq * H * d (q, o, dout, dq)
-  int64_t k_batch_stride;      // dense: Nk * H * d (k, v, dk, dv)
+  BwdStrides st[kBwdTensors];  // q, k, v, o, dout, dq, dk, dv
   int64_t lse_batch_stride;    // dense: H * Nq; varlen: 0
   int64_t lse_head_stride;     // dense: Nq; varlen: total
   int32_t Nq;                  // dense only
@@ -95,21 +105,33 @@ __device__ __forceinline__ float half_to_float(uint16_t b) {
   else return __uint_as_float((uint32_t)b << 16);
 }
 
-// D_i = dO_i . O_i for every row (token, head) of the launch, one row per
-// thread. Rows are numbered in memory order, row = token * H + head, with
-// token = b * N + n (dense) or the packed index (varlen, B = 1, N = total).
+// D_i = dO_i . O_i, fp32, for every row (token, head) of the launch, rows
+// numbered in the contiguous layout's memory order, row = token * H + head,
+// with token = b * N + n (dense) or the packed index (varlen: one batch of
+// N = total rows); nrows < 2^31. A row of d values is read by D/8 consecutive
+// lanes, 16 bytes each, so a wave's loads cover whole rows (coalesced, and
+// consecutive rows are adjacent in memory for contiguous tensors); the lanes'
+// partial sums meet in a butterfly of lane exchanges. O and dO are addressed
+// through their own (batch, token, head) strides.
+constexpr int kDeltaThreads = 256;
+
 template <int D, bool F16>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kDeltaThreads, kDeltaThreads)))
 void delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                  float* __restrict__ delta, int64_t nrows, int H, int N) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= nrows) return;
-  const u32x4* a = reinterpret_cast<const u32x4*>(o + row * D);
-  const u32x4* b = reinterpret_cast<const u32x4*>(dout + row * D);
+                  float* __restrict__ delta, int H, int N, int nrows, BwdStrides so,
+                  BwdStrides sd) {
+  constexpr int L = D / 8;                    // lanes per row
+  constexpr int R = kDeltaThreads / L;        // rows per workgroup
+  const int row = (int)blockIdx.x * R + (int)threadIdx.x / L;   // token * H + head
+  const int c = threadIdx.x % L;
+  const uint32_t token = (uint32_t)row / (uint32_t)H;
+  const int h = row - (int)token * H;
+  const uint32_t b = token / (uint32_t)N;
+  const int n = (int)(token - b * (uint32_t)N);
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 x = a[c], y = b[c];
+  if (row < nrows) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(o + b * so.b + n * so.t + h * so.h + 8 * c);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(dout + b * sd.b + n * sd.t + h * sd.h + 8 * c);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       acc = __builtin_fmaf(half_to_float<F16>((uint16_t)(x[w] & 0xffff)),
@@ -118,11 +140,9 @@ void delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ d
                            half_to_float<F16>((uint16_t)(y[w] >> 16)), acc);
     }
   }
-  const int64_t token = row / H;
-  const int head = (int)(row - token * H);
-  const int64_t bidx = token / N;
-  const int64_t n = token - bidx * N;
-  delta[(bidx * H + head) * N + n] = acc;
+#pragma unroll
+  for (int m = 1; m < L; m *= 2) acc += __shfl_xor(acc, m);
+  if (row < nrows && c == 0) delta[((int64_t)b * H + h) * N + n] = acc;
 }
 
 // Row-major LDS tile of kBwdTile rows, each padded to 2 D + 16 bytes, i.e.
@@ -217,32 +237,37 @@ __device__ __forceinline__ uint32_t gather_lane_bits(uint64_t kbits, int hi) {
 }
 
 // Work item of a workgroup: (128-row tile, head, batch or sequence) with the
-// tile index taken from blockIdx.x / units; offsets of the unit's rows.
+// tile index taken from blockIdx.x / units. seq is the batch index (dense) or
+// the sequence's first packed row (varlen); off(t) is the offset of tensor
+// t's first row of the unit, for that head.
+template <bool VARLEN>
 struct BwdUnit {
-  int tile, head, bidx, Nq, Nk;
-  int64_t q_off, k_off, l_off;
+  int tile, head, bidx, seq, Nq, Nk;
+  int64_t l_off;
+  __device__ __forceinline__ int64_t off(const BwdParams& p, int t) const {
+    return (int64_t)seq * (VARLEN ? p.st[t].t : p.st[t].b) + (int64_t)head * p.st[t].h;
+  }
 };
 
-__device__ __forceinline__ BwdUnit bwd_unit(const BwdParams& p, bool varlen, int D) {
-  BwdUnit u;
+template <bool VARLEN>
+__device__ __forceinline__ BwdUnit<VARLEN> bwd_unit(const BwdParams& p) {
+  BwdUnit<VARLEN> u;
   const int per = p.H * p.nbatch;
   u.tile = blockIdx.x / per;
   const int rem = blockIdx.x - u.tile * per;
   u.head = rem % p.H;
   u.bidx = rem / p.H;
-  if (varlen) {
+  if constexpr (VARLEN) {
     const int start = p.cu_seqlens[u.bidx];
     const int len = p.cu_seqlens[u.bidx + 1] - start;
+    u.seq = start;
     u.Nq = len;
     u.Nk = len;
-    u.q_off = (int64_t)start * p.row_stride + (int64_t)u.head * D;
-    u.k_off = u.q_off;
     u.l_off = (int64_t)u.head * p.lse_head_stride + start;
   } else {
+    u.seq = u.bidx;
     u.Nq = p.Nq;
     u.Nk = p.Nk;
-    u.q_off = (int64_t)u.bidx * p.q_batch_stride + (int64_t)u.head * D;
-    u.k_off = (int64_t)u.bidx * p.k_batch_stride + (int64_t)u.head * D;
     u.l_off = (int64_t)u.bidx * p.lse_batch_stride + (int64_t)u.head * p.lse_head_stride;
   }
   return u;
@@ -326,17 +351,19 @@ void dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   // Causal: key tiles in ascending order see the most queries first.
-  const BwdUnit u = bwd_unit(p, VARLEN, D);
+  const BwdUnit<VARLEN> u = bwd_unit<VARLEN>(p);
   const int k0 = u.tile * kBwdRows;
   if (k0 >= u.Nk) return;
-  const int rs = (int)p.row_stride;
+  const uint16_t* const gq = p.q + u.off(p, kTQ);
+  const uint16_t* const gdo = p.dout + u.off(p, kTdO);
+  const int rs_q = (int)p.st[kTQ].t, rs_do = (int)p.st[kTdO].t;
   const int kw0 = k0 + wave * 32;
   const int krow = kw0 + l32;
 
   bf16x8 kr[DS], vr[DS];
   if (krow < u.Nk) {
-    const u32x4* ks = reinterpret_cast<const u32x4*>(p.k + u.k_off + (int64_t)krow * rs);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(p.v + u.k_off + (int64_t)krow * rs);
+    const u32x4* ks = reinterpret_cast<const u32x4*>(p.k + u.off(p, kTK) + krow * p.st[kTK].t);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(p.v + u.off(p, kTV) + krow * p.st[kTV].t);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       kr[s] = __builtin_bit_cast(bf16x8, ks[2 * s + hi]);
@@ -418,9 +445,8 @@ void dkdv_kernel(BwdParams p) {
   // are used only in store_ld, after the tile's compute: a wait for them any
   // earlier would also wait for the tile copies issued before them.
   auto issue = [&](int qt, int b) __attribute__((always_inline)) {
-    copy_tile_async<D>(smem_lds + (2 * b) * TB, p.q + u.q_off, rs, qt * kBwdTile, u.Nq, wave, lane);
-    copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.dout + u.q_off, rs, qt * kBwdTile, u.Nq, wave,
-                       lane);
+    copy_tile_async<D>(smem_lds + (2 * b) * TB, gq, rs_q, qt * kBwdTile, u.Nq, wave, lane);
+    copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, gdo, rs_do, qt * kBwdTile, u.Nq, wave, lane);
   };
   struct Ld {
     float l, d;
@@ -553,8 +579,8 @@ void dkdv_kernel(BwdParams p) {
     __syncthreads();
   }
   if (krow < u.Nk) {
-    store_rowT<D, F16>(p.dk + u.k_off + (int64_t)krow * rs, dk, p.scale, hi);
-    store_rowT<D, F16>(p.dv + u.k_off + (int64_t)krow * rs, dv, 1.f, hi);
+    store_rowT<D, F16>(p.dk + u.off(p, kTdK) + krow * p.st[kTdK].t, dk, p.scale, hi);
+    store_rowT<D, F16>(p.dv + u.off(p, kTdV) + krow * p.st[kTdV].t, dv, 1.f, hi);
   }
 }
 
@@ -575,19 +601,21 @@ void dq_kernel(BwdParams p) {
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  BwdUnit u = bwd_unit(p, VARLEN, D);
+  BwdUnit<VARLEN> u = bwd_unit<VARLEN>(p);
   if (CAUSAL) u.tile = p.n_tiles - 1 - u.tile;   // longest rows first
   const int q0 = u.tile * kBwdRows;
   if (q0 >= u.Nq) return;
-  const int rs = (int)p.row_stride;
+  const uint16_t* const gk = p.k + u.off(p, kTK);
+  const uint16_t* const gv = p.v + u.off(p, kTV);
+  const int rs_k = (int)p.st[kTK].t, rs_v = (int)p.st[kTV].t;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
 
   bf16x8 qr[DS], dor[DS];
   float Lq = 0.f, Dq = 0.f;
   if (qrow < u.Nq) {
-    const u32x4* qs = reinterpret_cast<const u32x4*>(p.q + u.q_off + (int64_t)qrow * rs);
-    const u32x4* os = reinterpret_cast<const u32x4*>(p.dout + u.q_off + (int64_t)qrow * rs);
+    const u32x4* qs = reinterpret_cast<const u32x4*>(p.q + u.off(p, kTQ) + qrow * p.st[kTQ].t);
+    const u32x4* os = reinterpret_cast<const u32x4*>(p.dout + u.off(p, kTdO) + qrow * p.st[kTdO].t);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       qr[s] = __builtin_bit_cast(bf16x8, qs[2 * s + hi]);
@@ -666,8 +694,8 @@ void dq_kernel(BwdParams p) {
   const int n_iter = A + max(0, W1 - W0);
   auto tile_of = [&](int it) { return it < A ? it : W0 + (it - A); };
   auto issue = [&](int kt, int b) __attribute__((always_inline)) {
-    copy_tile_async<D>(smem_lds + (2 * b) * TB, p.k + u.k_off, rs, kt * kBwdTile, u.Nk, wave, lane);
-    copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, p.v + u.k_off, rs, kt * kBwdTile, u.Nk, wave,
+    copy_tile_async<D>(smem_lds + (2 * b) * TB, gk, rs_k, kt * kBwdTile, u.Nk, wave, lane);
+    copy_tile_async<D>(smem_lds + (2 * b + 1) * TB, gv, rs_v, kt * kBwdTile, u.Nk, wave,
                        lane);
     if constexpr (LOCAL) {
       if (tid < kBwdTile) {
@@ -786,7 +814,8 @@ void dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
   }
-  if (qrow < u.Nq) store_rowT<D, F16>(p.dq + u.q_off + (int64_t)qrow * rs, acc, p.scale, hi);
+  if (qrow < u.Nq)
+    store_rowT<D, F16>(p.dq + u.off(p, kTdQ) + qrow * p.st[kTdQ].t, acc, p.scale, hi);
 }
 
 }  // namespace fa

@@ -228,7 +228,8 @@ fa_status fa_fwd_padded(const void* q, const void* k, const void* v, void* o, fl
  * forward returned for the same q, k, v, scale and mask. Every element of dq,
  * dk, dv and delta is written.
  * Errors: as fa_fwd; an unknown dtype is FA_ERR_INVALID_ARGUMENT; H * d above
- * 2^24 is FA_ERR_UNSUPPORTED.
+ * 2^24, or B * Nq * H (varlen: total * H) above 2^31 - 1, is
+ * FA_ERR_UNSUPPORTED.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, float* delta, int32_t B,
@@ -403,6 +404,54 @@ fa_status fa_bwd_padded(const void* q, const void* k, const void* v, const void*
                         float* delta, const uint8_t* key_padding_mask, int32_t B, int32_t S,
                         int32_t H, int32_t d, int32_t dtype, float softmax_scale, int32_t causal,
                         void* stream);
+
+/*
+ * Backward pass on strided views: the general form of fa_bwd and
+ * fa_bwd_band, as fa_fwd_strided is of the forward, so that a model that
+ * keeps Q, K and V in one packed (B, S, 3, H, d) tensor (the layout of the
+ * unmasked path in "InternViT-6B-448px-V1-2 如何加速注意力计算", section
+ * FlashAttention 封装类三条执行路径) trains without copying them, and can
+ * write dQ, dK and dV straight into the matching views of a packed gradient.
+ *   q, k, v, o, dout, dq, dk, dv : views of the shapes of fa_bwd. Element
+ *       (b, n, h, e) of tensor X sits at X + b*sb + n*st + h*sh + e
+ *       (elements; d contiguous), with (sb, st, sh) X's entries of strides.
+ *   strides : HOST int64[24]: (batch, token, head) strides of q, k, v, o,
+ *       dout, dq, dk, dv, in that order. Every stride a multiple of 8 (rows
+ *       16-byte aligned), token strides at most 2^24. The outputs dq, dk, dv
+ *       must not overlap one another or any input.
+ *   lse, delta : (B, H, Nq) float32, contiguous, as in fa_bwd.
+ *   causal / window_left / window_right : as in fa_fwd_strided.
+ *   dtype, softmax_scale : as in fa_bwd.
+ * The results equal fa_bwd's (fa_bwd_band's) on contiguous copies of the
+ * same values, bit for bit.
+ * Errors: as fa_bwd and fa_bwd_band; a null stride array, a stride that is
+ * negative or not a multiple of 8, or causal with a window side other than -1
+ * is FA_ERR_INVALID_ARGUMENT; a token stride above 2^24 is
+ * FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, int32_t B, int32_t Nq, int32_t Nk, int32_t H, int32_t d,
+                         const int64_t* strides, int32_t dtype, float softmax_scale,
+                         int32_t causal, int32_t window_left, int32_t window_right,
+                         void* stream);
+
+/*
+ * Backward pass, packed variable-length batch on strided views: the general
+ * form of fa_bwd_varlen and fa_bwd_varlen_band. Row r (packed token index),
+ * head h, element e of tensor X sits at X + r*st + h*sh + e.
+ *   strides : HOST int64[16]: (token, head) strides of q, k, v, o, dout, dq,
+ *       dk, dv, in that order, with the rules of fa_bwd_strided.
+ * cu_seqlens, num_seqs, max_seqlen, total, lse and delta as in
+ * fa_bwd_varlen; the mask arguments as in fa_bwd_strided.
+ */
+fa_status fa_bwd_varlen_strided(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* delta, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t max_seqlen, int32_t total, int32_t H, int32_t d,
+                                const int64_t* strides, int32_t dtype, float softmax_scale,
+                                int32_t causal, int32_t window_left, int32_t window_right,
+                                void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int32_t status);

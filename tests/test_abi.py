@@ -255,6 +255,90 @@ def test_fa_fwd_varlen_strided_rejects_bad_arguments(kw, code):
     assert _varlen_strided(**kw) == code
 
 
+def _packed_bwd_strides(B, S, H, d, varlen=False):
+    """Strides of q, k, v (views of a packed (B, S, 3, H, d) tensor), o and dout
+    (contiguous) and dq, dk, dv (views of a packed gradient), flattened."""
+    t = 3 * H * d
+    packed = (S * t, t, d)[1 if varlen else 0:]
+    plain = (S * H * d, H * d, d)[1 if varlen else 0:]
+    return [x for s_ in (packed, packed, packed, plain, plain, packed, packed, packed) for x in s_]
+
+
+def _bwd_strided(**kw):
+    a = dict(q=P, k=P + 256, v=P + 512, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, delta=P, B=2, Nq=90,
+             Nk=90, H=2, d=64, st=_packed_bwd_strides(2, 90, 2, 64), dtype=_lib.FA_DTYPE_BF16,
+             scale=0.125, causal=1, left=-1, right=-1, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_bwd_strided(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
+                                   a["dk"], a["dv"], a["delta"], a["B"], a["Nq"], a["Nk"], a["H"],
+                                   a["d"], a["st"], a["dtype"], a["scale"], a["causal"], a["left"],
+                                   a["right"], a["stream"])
+
+
+def _bwd_varlen_strided(**kw):
+    a = dict(q=P, k=P + 256, v=P + 512, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, delta=P, cu=P,
+             num_seqs=2, max_seqlen=100, total=150, H=2, d=128,
+             st=_packed_bwd_strides(1, 150, 2, 128, varlen=True), dtype=_lib.FA_DTYPE_F16,
+             scale=0.1, causal=0, left=-1, right=-1, stream=None)
+    a.update(kw)
+    return _lib.raw_fa_bwd_varlen_strided(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"],
+                                          a["dq"], a["dk"], a["dv"], a["delta"], a["cu"],
+                                          a["num_seqs"], a["max_seqlen"], a["total"], a["H"],
+                                          a["d"], a["st"], a["dtype"], a["scale"], a["causal"],
+                                          a["left"], a["right"], a["stream"])
+
+
+def _with(st, i, value):
+    st = list(st)
+    st[i] = value
+    return st
+
+
+_BWD_ST = _packed_bwd_strides(2, 90, 2, 64)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(st=None), INV),
+    (dict(st=_with(_BWD_ST, 1, 3 * 2 * 64 + 4)), INV),        # q token stride not a multiple of 8
+    (dict(st=_with(_BWD_ST, 14, -8)), INV),                  # dout head stride negative
+    (dict(st=_with(_BWD_ST, 21, 1)), INV),                   # dv batch stride odd
+    (dict(st=_with(_BWD_ST, 19, (1 << 24) + 8)), UNS),       # dk token stride above 2^24
+    (dict(causal=1, left=4), INV),                           # causal with a window
+    (dict(causal=0, left=-2), INV), (dict(causal=2), INV),
+    (dict(causal=1, Nk=80), INV),                            # causal needs Nq == Nk
+    (dict(dtype=3), INV), (dict(d=256), UNS), (dict(d=48), UNS), (dict(B=0), INV),
+    (dict(dk=None), INV), (dict(v=P + 4), INV), (dict(scale=float("nan")), INV),
+    (dict(causal=0, left=3, Nq=(1 << 29) + 1, Nk=5), UNS),
+])
+def test_fa_bwd_strided_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _bwd_strided(**kw) == code
+    assert _lib.load().fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(st=None), INV), (dict(st=_with(_packed_bwd_strides(1, 150, 2, 128, True), 3, 130)), INV),
+    (dict(causal=1, right=0), INV), (dict(cu=None), INV), (dict(d=96), UNS), (dict(dtype=9), INV),
+    (dict(num_seqs=0), INV),
+])
+def test_fa_bwd_varlen_strided_rejects_bad_arguments(kw, code):
+    _lib_or_skip()
+    assert _bwd_varlen_strided(**kw) == code
+
+
+def test_bwd_strided_valid_calls_without_a_device_are_hip_errors():
+    _lib_or_skip()
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case covers hosts without one")
+    assert _bwd_strided() == HIP                                  # causal
+    assert _bwd_strided(causal=0, left=10, right=0) == HIP        # band
+    assert _bwd_strided(causal=0, Nq=30, dtype=_lib.FA_DTYPE_F16) == HIP
+    assert _bwd_strided(st=[0] * 24) == HIP                       # zero strides are allowed
+    assert _bwd_varlen_strided() == HIP
+    assert _bwd_varlen_strided(total=0, max_seqlen=0) == _lib.FA_OK
+
+
 def test_strided_valid_calls_without_a_device_are_hip_errors():
     _lib_or_skip()
     torch = pytest.importorskip("torch")
