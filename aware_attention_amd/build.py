@@ -32,6 +32,15 @@ SOURCES = ["fa_api.hip", "fa_bwd_api.hip", "fa_decode_api.hip", "fa_local_api.hi
            "fa_mx8_api.hip"]
 _NOISE = "is not a recognized feature for this target"
 
+# Per-source code generation flags. The backward's dK/dV kernel holds its dK
+# and dV accumulators and its S and dP tiles at once (one wave per SIMD, up
+# to 512 registers); with MFMA results placed in the accumulation registers
+# by default, the register allocator shares them between the two and moves
+# 128 accumulators out and back every tile. The vector-register form puts
+# MFMA results in the arch VGPRs, so the accumulation registers hold the
+# rest without copies.
+SOURCE_FLAGS = {"fa_bwd_api.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def hipcc_compile(src: str, obj: str, extra=()) -> list[str]:
     return [HIPCC, *DEVICE_FLAGS, "-fPIC", "-c", "-Wall",
@@ -47,7 +56,7 @@ def build(verbose: bool = True, stress: bool = False) -> str:
     suffix = "_stress" if stress else ""
     objs = [os.path.join(CSRC, os.path.splitext(s)[0] + suffix + ".o") for s in SOURCES]
     extra = ["-DFA_STRESS"] if stress else []
-    cmds = [hipcc_compile(s, o, extra) for s, o in zip(SOURCES, objs)]
+    cmds = [hipcc_compile(s, o, [*extra, *SOURCE_FLAGS.get(s, [])]) for s, o in zip(SOURCES, objs)]
     procs = []
     for cmd in cmds:
         if verbose:

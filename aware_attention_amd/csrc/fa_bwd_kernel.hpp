@@ -98,6 +98,12 @@ constexpr float kLog2eF = 1.44269504088896340736f;
 // and both accumulators in up to 512 registers.
 template <int D, bool LOCAL>
 constexpr int kDkdvWaves = (D == 32 || (D == 64 && !LOCAL)) ? 2 : 1;
+// LDS operand reads the dK/dV kernel keeps in flight ahead of its products
+// where it runs one wave per SIMD (nothing else there hides the LDS latency
+// of each product's operand); 0: each read next to its product, where a
+// second wave on the SIMD covers it and the registers are needed.
+template <int D, bool LOCAL>
+constexpr int kDkdvRing = kDkdvWaves<D, LOCAL> == 1 ? 8 : 0;
 
 template <bool F16>
 __device__ __forceinline__ float half_to_float(uint16_t b) {
@@ -508,15 +514,67 @@ void dkdv_kernel(BwdParams p) {
     if (useful) {
 
     // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys.
+    constexpr int RING = kDkdvRing<D, LOCAL>;
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    // L and D of the 4 queries of each (qb, t, half) group this lane needs
+    // (read here, ahead of the products, when the ring is on).
+    float4 L4s[8], D4s[8];
+    auto ld_group = [&](int g) __attribute__((always_inline)) {
+      const int q4 = 8 * g + 4 * hi;   // g = 4 qb + 2 t + half: 32 qb + 16 t + 8 half
+      L4s[g] = *reinterpret_cast<const float4*>(l_lds + q4);
+      D4s[g] = *reinterpret_cast<const float4*>(d_lds + q4);
+    };
+    if constexpr (RING > 0) {
+      // Step st = 4 ds + 2 qb + (0: S from Q, 1: dP from dO); the operands
+      // go through a ring of RING registers, each read issued that many
+      // products ahead (sched_barrier keeps reads and products in order and
+      // lets only ALU work cross).
+      constexpr int NS = 4 * DS;
+      auto rd = [&](int st) __attribute__((always_inline)) {
+        return lds16((st & 1) ? do_lds : q_lds, ((st >> 1) & 1) * 32 * RBP + ln.row_rd + (st >> 2) * 32);
+      };
+      bf16x8 ra[RING];
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
+      for (int st = 0; st < RING; ++st) ra[st] = rd(st);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int off = qb * 32 * RBP + ln.row_rd + ds * 32;
-        s[qb] = mfma32<F16>(lds16(q_lds, off), kr[ds], s[qb]);
-        dp[qb] = mfma32<F16>(lds16(do_lds, off), vr[ds], dp[qb]);
+      for (int g = 0; g < 8; ++g) ld_group(g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 a = ra[st % RING];
+        if (st + RING < NS) ra[st % RING] = rd(st + RING);
+        const int ds = st >> 2, qb = (st >> 1) & 1;
+        if (st & 1) dp[qb] = mfma32<F16>(a, vr[ds], dp[qb]);
+        else s[qb] = mfma32<F16>(a, kr[ds], s[qb]);
+        __builtin_amdgcn_sched_barrier(0x7);
       }
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int off = qb * 32 * RBP + ln.row_rd + ds * 32;
+          s[qb] = mfma32<F16>(lds16(q_lds, off), kr[ds], s[qb]);
+          dp[qb] = mfma32<F16>(lds16(do_lds, off), vr[ds], dp[qb]);
+        }
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS: step st = 2 (DB (2 qb + t) + b) +
+    // (0: dV from dO, 1: dK from Q), A operands by transposing reads. With the
+    // ring on, its first reads are issued here, so that their latency hides
+    // behind the exponentials below.
+    constexpr int NP = 8 * DB;
+    constexpr int RING2 = RING > 0 ? RING : 1;
+    auto rd2 = [&](int st) __attribute__((always_inline)) {
+      const int which = st & 1, b = (st >> 1) % DB, c = (st >> 1) / DB;   // c = 2 qb + t
+      const int r0 = 16 * c * RBP;
+      return lds_tr8(which ? q_lds : do_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]);
+    };
+    bf16x8 rb[RING2];
+    if constexpr (RING > 0) {
+#pragma unroll
+      for (int st = 0; st < RING; ++st) rb[st] = rd2(st);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // P = exp2(scale log2e S - L log2e) and dS = P (dP - D), packed as B operands.
     bf16x8 pb[2][2], dsb[2][2];
@@ -527,9 +585,10 @@ void dkdv_kernel(BwdParams p) {
         u32x4 wp, wd;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {   // registers 8t + 4 half + 0..3
-          const int q4 = 32 * qb + 16 * t + 8 * half + 4 * hi;     // first of 4 queries
-          const float4 L4 = *reinterpret_cast<const float4*>(l_lds + q4);
-          const float4 D4 = *reinterpret_cast<const float4*>(d_lds + q4);
+          const int g = 4 * qb + 2 * t + half;
+          const int q4 = 8 * g + 4 * hi;      // first of 4 queries
+          if constexpr (RING == 0) ld_group(g);
+          const float4 L4 = L4s[g], D4 = D4s[g];
           const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
           i32x4 qmr = {0, 0, 0, 0}, qmc = {0, 0, 0, 0};
           if constexpr (LOCAL) {
@@ -559,17 +618,22 @@ void dkdv_kernel(BwdParams p) {
         dsb[qb][t] = __builtin_bit_cast(bf16x8, wd);
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS.
+    if constexpr (RING > 0) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      for (int st = 0; st < NP; ++st) {
+        const bf16x8 a = rb[st % RING];
+        if (st + RING < NP) rb[st % RING] = rd2(st + RING);
+        const int b = (st >> 1) % DB, c = (st >> 1) / DB, qb = c >> 1, t = c & 1;
+        if (st & 1) dk[b] = mfma32<F16>(a, dsb[qb][t], dk[b]);
+        else dv[b] = mfma32<F16>(a, pb[qb][t], dv[b]);
+        __builtin_amdgcn_sched_barrier(0x7);
+      }
+    } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r0 = (32 * qb + 16 * t) * RBP;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          dv[b] = mfma32<F16>(lds_tr8(do_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), pb[qb][t], dv[b]);
-          dk[b] = mfma32<F16>(lds_tr8(q_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]), dsb[qb][t], dk[b]);
-        }
+      for (int st = 0; st < NP; ++st) {
+        const int b = (st >> 1) % DB, c = (st >> 1) / DB, qb = c >> 1, t = c & 1;
+        if (st & 1) dk[b] = mfma32<F16>(rd2(st), dsb[qb][t], dk[b]);
+        else dv[b] = mfma32<F16>(rd2(st), pb[qb][t], dv[b]);
       }
     }
     }
