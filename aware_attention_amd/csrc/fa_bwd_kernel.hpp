@@ -101,9 +101,12 @@ constexpr int kDkdvWaves = (D == 32 || (D == 64 && !LOCAL)) ? 2 : 1;
 // LDS operand reads the dK/dV kernel keeps in flight ahead of its products
 // where it runs one wave per SIMD (nothing else there hides the LDS latency
 // of each product's operand); 0: each read next to its product, where a
-// second wave on the SIMD covers it and the registers are needed.
-template <int D, bool LOCAL>
-constexpr int kDkdvRing = kDkdvWaves<D, LOCAL> == 1 ? 8 : 0;
+// second wave on the SIMD covers it and the registers are needed. Unmasked
+// attention takes a deeper ring than the masked kinds, whose mask arithmetic
+// needs the registers (measured at d = 128: 12 vs 8 is +5.5 % unmasked and
+// -4 to -7 % causal or banded).
+template <int D, bool LOCAL, bool MASKED>
+constexpr int kDkdvRing = kDkdvWaves<D, LOCAL> == 1 ? (MASKED ? 8 : 12) : 0;
 
 template <bool F16>
 __device__ __forceinline__ float half_to_float(uint16_t b) {
@@ -514,7 +517,7 @@ void dkdv_kernel(BwdParams p) {
     if (useful) {
 
     // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys.
-    constexpr int RING = kDkdvRing<D, LOCAL>;
+    constexpr int RING = kDkdvRing<D, LOCAL, CAUSAL || BAND || KPM || LOCAL>;
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
     // L and D of the 4 queries of each (qb, t, half) group this lane needs
     // (read here, ahead of the products, when the ring is on).
