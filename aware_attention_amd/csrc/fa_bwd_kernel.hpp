@@ -579,8 +579,14 @@ void dkdv_kernel(BwdParams p) {
       for (int st = 0; st < RING; ++st) rb[st] = rd2(st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // P = exp2(scale log2e S - L log2e) and dS = P (dP - D), packed as B operands.
+    // P = exp2(scale log2e S - L log2e) and dS = P (dP - D), packed as B
+    // operands; masked: with the per-pair mask test, which tiles where every
+    // (query, key) pair of the wave is visible skip (below the diagonal,
+    // inside the band, all of the wave's keys valid; padding queries have
+    // L = +inf, queries past the end a copy of the last row and L = +inf).
     bf16x8 pb[2][2], dsb[2][2];
+    auto pds = [&](auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -603,11 +609,14 @@ void dkdv_kernel(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * t + 4 * half + e;
             const int qi = qb0 + q4 + e;
-            bool ok = (!CAUSAL || krow <= qi) && k_valid;
-            if constexpr (BAND) ok = ok && krow >= qi + band_lo && krow <= qi + band_hi;
-            if constexpr (LOCAL)
-              ok = ok & (map_near(qmr[e], qmc[e], kmr, kmc, WR, WC) | (qmr[e] == kKeyAnchor) |
-                         (kmr == kKeyAnchor));
+            bool ok = true;
+            if constexpr (masked) {
+              ok = (!CAUSAL || krow <= qi) && k_valid;
+              if constexpr (BAND) ok = ok && krow >= qi + band_lo && krow <= qi + band_hi;
+              if constexpr (LOCAL)
+                ok = ok & (map_near(qmr[e], qmc[e], kmr, kmc, WR, WC) | (qmr[e] == kKeyAnchor) |
+                           (kmr == kKeyAnchor));
+            }
             const float pe = ok ? __builtin_amdgcn_exp2f(s[qb][r] * p.scale_log2 - Lv[e]) : 0.f;
             pv[e] = pe;
             dsv[e] = pe * (dp[qb][r] - Dv[e]);
@@ -621,6 +630,15 @@ void dkdv_kernel(BwdParams p) {
         dsb[qb][t] = __builtin_bit_cast(bf16x8, wd);
       }
     }
+    };
+    // (Causal tiles keep the test: at d = 128 the two instantiations cost the
+    // causal dK/dV loop more than the test itself, prefill shapes -2 to -3 %.)
+    bool full = !CAUSAL;
+    if constexpr (BAND) full = kw0 >= qb0 + kBwdTile - 1 + band_lo && kw0 + 31 <= qb0 + band_hi;
+    if constexpr (KPM) full = full && __builtin_amdgcn_ballot_w64(k_valid) == ~0ull;
+    if constexpr (LOCAL) full = false;
+    if (full) pds(std::false_type{});
+    else pds(std::true_type{});
     if constexpr (RING > 0) {
 #pragma unroll
       for (int st = 0; st < NP; ++st) {
@@ -819,8 +837,13 @@ void dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0x7);
       }
     }
-    // dS^T = P^T (dP^T - D), packed as B operands.
+    // dS^T = P^T (dP^T - D), packed as B operands; masked: with the
+    // per-pair mask test, which tiles where every (query, key) pair of the
+    // wave is visible skip (no key past the end, below the diagonal, inside
+    // the band, all keys valid).
     bf16x8 dsb[2][2];
+    auto pds = [&](auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -832,7 +855,7 @@ void dq_kernel(BwdParams p) {
           // Map positions of this pair's keys (key index 4 (r/4)-aligned group).
           const int kk = 32 * kb + 8 * ((8 * t + 2 * i) >> 2) + 4 * hi;
           i32x4 kmr = {0, 0, 0, 0}, kmc = {0, 0, 0, 0};
-          if constexpr (LOCAL) {
+          if constexpr (LOCAL && masked) {
             kmr = *reinterpret_cast<const i32x4*>(&kmap[buf * 2 * kBwdTile + kk]);
             kmc = *reinterpret_cast<const i32x4*>(&kmap[buf * 2 * kBwdTile + kBwdTile + kk]);
           }
@@ -840,13 +863,16 @@ void dq_kernel(BwdParams p) {
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * t + 2 * i + e;
             const int key = kb0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            bool ok = key < u.Nk && (!CAUSAL || key <= qrow);
-            if constexpr (BAND) ok = ok && key >= qrow + band_lo && key <= qrow + band_hi;
-            if constexpr (KPM) ok = ok && ((kvalid >> (16 * kb + r)) & 1);
-            if constexpr (LOCAL) {
-              const int j = r & 3;   // position of the key in its group of 4
-              ok = ok & (map_near(qmr, qmc, kmr[j], kmc[j], WR, WC) | (qmr == kKeyAnchor) |
-                         (kmr[j] == kKeyAnchor));
+            bool ok = true;
+            if constexpr (masked) {
+              ok = key < u.Nk && (!CAUSAL || key <= qrow);
+              if constexpr (BAND) ok = ok && key >= qrow + band_lo && key <= qrow + band_hi;
+              if constexpr (KPM) ok = ok && ((kvalid >> (16 * kb + r)) & 1);
+              if constexpr (LOCAL) {
+                const int j = r & 3;   // position of the key in its group of 4
+                ok = ok & (map_near(qmr, qmc, kmr[j], kmc[j], WR, WC) | (qmr == kKeyAnchor) |
+                           (kmr[j] == kKeyAnchor));
+              }
             }
             const float pe = ok ? __builtin_amdgcn_exp2f(s[kb][r] * p.scale_log2 - Lq) : 0.f;
             v2[e] = pe * (dp[kb][r] - Dq);
@@ -856,6 +882,15 @@ void dq_kernel(BwdParams p) {
         dsb[kb][t] = __builtin_bit_cast(bf16x8, w);
       }
     }
+    };
+    bool full = kb0 + kBwdTile <= u.Nk;
+    if constexpr (CAUSAL) full = full && kb0 + kBwdTile - 1 <= qw0;
+    if constexpr (BAND)
+      full = full && kb0 >= qw0 + 31 + band_lo && kb0 + kBwdTile - 1 <= qw0 + band_hi;
+    if constexpr (KPM) full = full && __builtin_amdgcn_ballot_w64(kvalid != ~0u) == 0;
+    if constexpr (LOCAL) full = false;
+    if (full) pds(std::false_type{});
+    else pds(std::true_type{});
     // dQ^T += K^T dS^T, with the same read-ahead (step st = g DB + b, g = 2 kb + t).
     {
       constexpr int NP = 4 * DB;
