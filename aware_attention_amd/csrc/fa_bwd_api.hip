@@ -29,8 +29,9 @@ hipError_t launch_bwd_t(const fa::BwdParams& p, int64_t nrows, int N, uint32_t g
                      p.st[fa::kTO], p.st[fa::kTdO]);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>), dim3(grid_k),
-                     dim3(fa::kBwdThreads), 0, stream, p);
+  // d = 256: two dK/dV workgroups per key tile, one per half of the head dimension.
+  hipLaunchKernelGGL((fa::dkdv_kernel<D, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>),
+                     dim3(D == 256 ? 2 * grid_k : grid_k), dim3(fa::kBwdThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   fa::BwdParams pq = p;
@@ -50,6 +51,9 @@ hipError_t launch_bwd_d(const fa::BwdParams& p, int d, int64_t nrows, int N, uin
     case 64:
       return launch_bwd_t<64, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>(p, nrows, N, grid_k, grid_q,
                                                                    stream);
+    case 256:
+      return launch_bwd_t<256, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>(p, nrows, N, grid_k, grid_q,
+                                                                    stream);
     default:
       return launch_bwd_t<128, CAUSAL, VARLEN, F16, BAND, KPM, LOCAL>(p, nrows, N, grid_k, grid_q,
                                                                     stream);
@@ -115,7 +119,8 @@ fa_status check_bwd_common(int32_t H, int32_t d, int32_t dtype, float scale, int
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
+  if (d != 32 && d != 64 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim must be 32, 64, 128 or 256");
   return FA_OK;
 }
 
@@ -198,7 +203,7 @@ fa_status dense_bwd(const void* q, const void* k, const void* v, const void* o, 
   const int64_t grid_q = (Nq + fa::kBwdRows - 1) / fa::kBwdRows * units;
   const int64_t nrows = (int64_t)B * Nq * H;
   // (the D = dO . O launch numbers its rows with 32-bit integers)
-  if (grid_k > INT32_MAX || grid_q > INT32_MAX || nrows > INT32_MAX)
+  if (grid_k * (d == 256 ? 2 : 1) > INT32_MAX || grid_q > INT32_MAX || nrows > INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "too many tiles or rows (B * N * H above 2^31 - 1) for one launch");
   st = check_device();
   if (st != FA_OK) return st;
@@ -275,7 +280,7 @@ fa_status varlen_bwd(const void* q, const void* k, const void* v, const void* o,
   const int64_t n_t = (max_seqlen + fa::kBwdRows - 1) / fa::kBwdRows;
   const int64_t grid = n_t * units;
   const int64_t nrows = (int64_t)total * H;
-  if (grid > INT32_MAX || nrows > INT32_MAX)
+  if (grid * (d == 256 ? 2 : 1) > INT32_MAX || nrows > INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "too many tiles or rows (B * N * H above 2^31 - 1) for one launch");
   st = check_device();
   if (st != FA_OK) return st;

@@ -246,7 +246,8 @@ __device__ __forceinline__ uint32_t gather_lane_bits(uint64_t kbits, int hi) {
 }
 
 // Work item of a workgroup: (128-row tile, head, batch or sequence) with the
-// tile index taken from blockIdx.x / units. seq is the batch index (dense) or
+// tile index taken from bid / units (bid: the workgroup's index in the grid,
+// without the d-half bit of the d = 256 dK/dV launch). seq is the batch index (dense) or
 // the sequence's first packed row (varlen); off(t) is the offset of tensor
 // t's first row of the unit, for that head.
 template <bool VARLEN>
@@ -259,11 +260,11 @@ struct BwdUnit {
 };
 
 template <bool VARLEN>
-__device__ __forceinline__ BwdUnit<VARLEN> bwd_unit(const BwdParams& p) {
+__device__ __forceinline__ BwdUnit<VARLEN> bwd_unit(const BwdParams& p, int bid) {
   BwdUnit<VARLEN> u;
   const int per = p.H * p.nbatch;
-  u.tile = blockIdx.x / per;
-  const int rem = blockIdx.x - u.tile * per;
+  u.tile = bid / per;
+  const int rem = bid - u.tile * per;
   u.head = rem % p.H;
   u.bidx = rem / p.H;
   if constexpr (VARLEN) {
@@ -360,7 +361,13 @@ void dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   // Causal: key tiles in ascending order see the most queries first.
-  const BwdUnit<VARLEN> u = bwd_unit<VARLEN>(p);
+  // d = 256: each workgroup accumulates dK and dV for one half of the head
+  // dimension (columns 128 half ..; blockIdx.x = 2 bid + half) and
+  // recomputes S and dP over the full d; otherwise all of it (half = 0).
+  constexpr int DV = D == 256 ? 128 : D;   // dK/dV columns of a workgroup
+  constexpr int DBV = DV / 32;
+  const int half = D == 256 ? (int)(blockIdx.x & 1) : 0;
+  const BwdUnit<VARLEN> u = bwd_unit<VARLEN>(p, D == 256 ? (int)(blockIdx.x >> 1) : (int)blockIdx.x);
   const int k0 = u.tile * kBwdRows;
   if (k0 >= u.Nk) return;
   const uint16_t* const gq = p.q + u.off(p, kTQ);
@@ -383,9 +390,9 @@ void dkdv_kernel(BwdParams p) {
     for (int s = 0; s < DS; ++s) kr[s] = vr[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
   const BwdLanes<D> ln(lane);
-  f32x16 dk[DB], dv[DB];
+  f32x16 dk[DBV], dv[DBV];
 #pragma unroll
-  for (int b = 0; b < DB; ++b) dk[b] = dv[b] = f32x16{};
+  for (int b = 0; b < DBV; ++b) dk[b] = dv[b] = f32x16{};
 
   int n_qt = (u.Nq + kBwdTile - 1) / kBwdTile;
   int qt0 = CAUSAL ? k0 / kBwdTile : 0;
@@ -562,16 +569,16 @@ void dkdv_kernel(BwdParams p) {
         }
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS: step st = 2 (DB (2 qb + t) + b) +
-    // (0: dV from dO, 1: dK from Q), A operands by transposing reads. With the
-    // ring on, its first reads are issued here, so that their latency hides
-    // behind the exponentials below.
-    constexpr int NP = 8 * DB;
+    // dV^T += dO^T P and dK^T += Q^T dS: step st = 2 (DBV (2 qb + t) + b) +
+    // (0: dV from dO, 1: dK from Q), A operands by transposing reads of the
+    // workgroup's columns. With the ring on, its first reads are issued here,
+    // so that their latency hides behind the exponentials below.
+    constexpr int NP = 8 * DBV;
     constexpr int RING2 = RING > 0 ? RING : 1;
     auto rd2 = [&](int st) __attribute__((always_inline)) {
-      const int which = st & 1, b = (st >> 1) % DB, c = (st >> 1) / DB;   // c = 2 qb + t
-      const int r0 = 16 * c * RBP;
-      return lds_tr8(which ? q_lds : do_lds, r0 + ln.tr_rd[b], r0 + 8 * RBP + ln.tr_rd[b]);
+      const int which = st & 1, b = (st >> 1) % DBV, c = (st >> 1) / DBV;   // c = 2 qb + t
+      const int r0 = 16 * c * RBP, tr = ln.tr_rd[b + DBV * half];
+      return lds_tr8(which ? q_lds : do_lds, r0 + tr, r0 + 8 * RBP + tr);
     };
     bf16x8 rb[RING2];
     if constexpr (RING > 0) {
@@ -644,7 +651,7 @@ void dkdv_kernel(BwdParams p) {
       for (int st = 0; st < NP; ++st) {
         const bf16x8 a = rb[st % RING];
         if (st + RING < NP) rb[st % RING] = rd2(st + RING);
-        const int b = (st >> 1) % DB, c = (st >> 1) / DB, qb = c >> 1, t = c & 1;
+        const int b = (st >> 1) % DBV, c = (st >> 1) / DBV, qb = c >> 1, t = c & 1;
         if (st & 1) dk[b] = mfma32<F16>(a, dsb[qb][t], dk[b]);
         else dv[b] = mfma32<F16>(a, pb[qb][t], dv[b]);
         __builtin_amdgcn_sched_barrier(0x7);
@@ -652,7 +659,7 @@ void dkdv_kernel(BwdParams p) {
     } else {
 #pragma unroll
       for (int st = 0; st < NP; ++st) {
-        const int b = (st >> 1) % DB, c = (st >> 1) / DB, qb = c >> 1, t = c & 1;
+        const int b = (st >> 1) % DBV, c = (st >> 1) / DBV, qb = c >> 1, t = c & 1;
         if (st & 1) dk[b] = mfma32<F16>(rd2(st), dsb[qb][t], dk[b]);
         else dv[b] = mfma32<F16>(rd2(st), pb[qb][t], dv[b]);
       }
@@ -664,15 +671,15 @@ void dkdv_kernel(BwdParams p) {
     __syncthreads();
   }
   if (krow < u.Nk) {
-    store_rowT<D, F16>(p.dk + u.off(p, kTdK) + krow * p.st[kTdK].t, dk, p.scale, hi);
-    store_rowT<D, F16>(p.dv + u.off(p, kTdV) + krow * p.st[kTdV].t, dv, 1.f, hi);
+    store_rowT<DV, F16>(p.dk + u.off(p, kTdK) + krow * p.st[kTdK].t + DV * half, dk, p.scale, hi);
+    store_rowT<DV, F16>(p.dv + u.off(p, kTdV) + krow * p.st[kTdV].t + DV * half, dv, 1.f, hi);
   }
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool F16, bool BAND = false, bool KPM = false,
           bool LOCAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
-                          amdgpu_waves_per_eu(2, 2)))
+                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void dq_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
@@ -686,7 +693,7 @@ void dq_kernel(BwdParams p) {
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  BwdUnit<VARLEN> u = bwd_unit<VARLEN>(p);
+  BwdUnit<VARLEN> u = bwd_unit<VARLEN>(p, (int)blockIdx.x);
   if (CAUSAL) u.tile = p.n_tiles - 1 - u.tile;   // longest rows first
   const int q0 = u.tile * kBwdRows;
   if (q0 >= u.Nq) return;

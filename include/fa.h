@@ -27,8 +27,8 @@
  *     The library keeps no pointer after it returns and allocates no memory.
  *   - Q, K, V and O are bfloat16 (passed as void*), or fp16 where the
  *     *_strided entry points say so; L is float32.
- *   - Head dimension d must be 32, 64, 128 or 256 in the forward entry
- *     points (every mask), 32, 64 or 128 in the backward.
+ *   - Head dimension d must be 32, 64, 128 or 256 (every entry point and
+ *     mask, the FP8 path aside).
  *   - softmax_scale may be any finite value, 0 and negative values included
  *     (callers normally pass 1/sqrt(d)); L is computed on the scaled scores.
  *   - causal = 1 applies the lower-triangular mask of self-attention (query i
@@ -224,6 +224,11 @@ fa_status fa_fwd_padded(const void* q, const void* k, const void* v, void* o, fl
  *   dtype          : FA_DTYPE_BF16 or FA_DTYPE_F16 for q, k, v, o, dout, dq,
  *                    dk, dv; P and dS enter the matrix cores in that type
  *   causal         : as in fa_fwd (Nq == Nk)
+ *   d              : 32, 64, 128 or 256 ("FlashAttention/zh", section
+ *                    局限性, puts the fused kernel's reach at head
+ *                    dimensions up to about 256). At 256 the dK/dV pass runs two workgroups per
+ *                    key tile, one per half of the head dimension, each
+ *                    recomputing S and dP over the full d.
  * All tensors densely packed and 16-byte aligned; o and lse are those the
  * forward returned for the same q, k, v, scale and mask. Every element of dq,
  * dk, dv and delta is written.

@@ -306,7 +306,7 @@ _BWD_ST = _packed_bwd_strides(2, 90, 2, 64)
     (dict(causal=1, left=4), INV),                           # causal with a window
     (dict(causal=0, left=-2), INV), (dict(causal=2), INV),
     (dict(causal=1, Nk=80), INV),                            # causal needs Nq == Nk
-    (dict(dtype=3), INV), (dict(d=256), UNS), (dict(d=48), UNS), (dict(B=0), INV),
+    (dict(dtype=3), INV), (dict(d=512), UNS), (dict(d=48), UNS), (dict(B=0), INV),
     (dict(dk=None), INV), (dict(v=P + 4), INV), (dict(scale=float("nan")), INV),
     (dict(causal=0, left=3, Nq=(1 << 29) + 1, Nk=5), UNS),
 ])
@@ -448,12 +448,17 @@ def test_padded_valid_call_without_a_device_is_a_hip_error():
 
 def test_head_dim_256_checks():
     """d = 256 runs every forward mask (unmasked, causal, varlen, bands,
-    padding masks); the backward rejects it on the host."""
+    padding masks) and the backward's; other head dimensions are refused."""
     _lib_or_skip()
-    assert _bwd(d=256) == UNS
+    for d in (16, 96, 192, 512):
+        assert _bwd(d=d) == UNS
+        assert _bwd_varlen(d=d) == UNS
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         return
+    assert _bwd(d=256) == HIP and _bwd(d=256, causal=1, dtype=_lib.FA_DTYPE_F16) == HIP
+    assert _bwd_varlen(d=256) == HIP
+    assert _bwd_strided(d=256, st=_packed_bwd_strides(2, 90, 2, 256)) == HIP
     assert _fwd(d=256) == HIP and _fwd(d=256, causal=1) == HIP
     assert _varlen(d=256) == HIP
     assert _band(d=256) == HIP
@@ -565,7 +570,7 @@ def test_bwd_local_argument_checks():
     assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 0, 2, 2, None) == INV
     assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 0, 4, 10, -1, 2, None) == INV
     assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 64, bf, 0.1, 2, 4, 10, 2, 2, None) == INV
-    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 256, bf, 0.1, 0, 4, 10, 2, 2, None) == UNS
+    assert lib.raw_fa_bwd_local(*args, 1, 100, 2, 192, bf, 0.1, 0, 4, 10, 2, 2, None) == UNS
     assert lib.raw_fa_bwd_local(*args, 1, (1 << 28) + 1, 2, 64, bf, 0.1, 0, 4, 10, 2, 2,
                                 None) == UNS
     torch = pytest.importorskip("torch")

@@ -125,14 +125,14 @@ def check_bwd_dense(B, Nq, Nk, H, d, causal, seed, dtype="bf16", scale=None):
     assert_grad_close(_np(delta), gd, "delta " + what, per_row=False, extra=dD)
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 65, 200])
 def test_bwd_dense(d, causal, N):
     check_bwd_dense(2, N, N, 2, d, causal, seed=8000 + N + d)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("Nq,Nk", [(129, 300), (300, 129), (1, 77)])
 def test_bwd_cross_lengths(d, Nq, Nk):
     check_bwd_dense(1, Nq, Nk, 2, d, False, seed=8100 + Nq + d)
@@ -144,19 +144,20 @@ def test_bwd_long_rows(causal):
     check_bwd_dense(1, 700, 700, 2, 128, causal, seed=8200)
 
 
-@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("d", [32, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_f16(d, causal):
     check_bwd_dense(2, 333, 333, 2, d, causal, seed=8300 + d, dtype="f16")
 
 
+@pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_varlen(causal):
+def test_bwd_varlen(causal, d):
     import aware_attention_amd as aa
     torch = torch_or_skip()
     lengths = [1, 127, 0, 200, 64, 300]
-    H, d = 2, 64
-    say(f"bwd varlen lengths={lengths} causal={causal}")
+    H = 2
+    say(f"bwd varlen lengths={lengths} causal={causal} d={d}")
     q, k, v, cu = W.make_varlen(lengths, H, d, seed=8400)
     do, _, _, _ = W.make_varlen(lengths, H, d, seed=8401)
     scale = 1 / np.sqrt(d)
@@ -296,7 +297,7 @@ def check_bwd_band(B, Nq, Nk, H, d, window, seed):
     assert_grad_close(_np(delta), gd, "delta " + what, per_row=False, extra=dD)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("window", [(None, 0), (16, 16), (100, 3), (0, None), (0, 0)])
 @pytest.mark.parametrize("Nq,Nk", [(333, 333), (129, 300), (300, 129)])
 def test_bwd_band(d, window, Nq, Nk):
@@ -338,7 +339,7 @@ def test_bwd_band_varlen():
     assert_grad_close(_np(dv), gv, "band varlen dv")
 
 
-@pytest.mark.parametrize("d,S", [(64, 333), (128, 333), (128, 1025)])
+@pytest.mark.parametrize("d,S", [(64, 333), (128, 333), (128, 1025), (256, 333)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_padded(d, S, causal):
     # Masks: right padding, scattered holes, all valid, all padding, a middle
@@ -435,7 +436,7 @@ def check_bwd_local(B, N, H, d, G, Wd, win, causal, seed):
     assert_grad_close(_np(dv), gv, "dv " + what)
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_local_detector_map(d, causal):
     # 8 anchors + a 20 x 20 map, 5 x 5 window.
@@ -478,7 +479,8 @@ def test_autograd_with_local_pattern():
 # Full-size backward of every timed workload, in the launch bench.py times
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["prefill8k", "vit", "det1600", "band8k", "vitpad", "detlocal"])
+@pytest.mark.parametrize("name", ["prefill8k", "vit", "det1600", "band8k", "vitpad", "detlocal",
+                                  "prefill8k_d256", "band8k_d256"])
 def test_bwd_full_size_workloads(name):
     """Whole (batch, head) pairs against the oracle's gradients (one pair at
     N = 8192, two elsewhere), and at every head the key-shift invariant (the

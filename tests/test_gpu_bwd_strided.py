@@ -31,7 +31,7 @@ def _mask_kw(mask):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("mask", ["none", "causal", "band"])
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_bwd_packed_qkv_dense(dtype, mask, d):
     """q, k, v views of a (B, S, 3, H, d) tensor, dout a (B, H, S, d) tensor seen as
     (B, S, H, d), dq, dk, dv written into the views of a packed (B, S, 3, H, d)
