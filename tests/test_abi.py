@@ -716,3 +716,54 @@ def test_decode_noalloc_valid_call_without_a_device_is_a_hip_error():
         pytest.skip("a GPU is present; this case covers hosts without one")
     assert _decode_noalloc() == HIP
     assert _decode_noalloc(d=32, sl=P, dtype=_lib.FA_DTYPE_F16) == HIP
+
+
+def test_backward_gradient_views_on_another_device_are_refused(host_as_gpu):
+    """Caller-supplied dq/dk/dv may be strided views, but still only on q's device."""
+    torch = host_as_gpu
+    B, N, H, d = 1, 16, 2, 64
+    packed = torch.zeros(B, N, 3, H, d, dtype=torch.bfloat16)
+    q, k, v = packed.unbind(2)
+    o, do = torch.zeros(B, N, H, d, dtype=torch.bfloat16), torch.zeros(B, N, H, d, dtype=torch.bfloat16)
+    lse = torch.zeros(B, H, N)
+    meta = _meta(torch, (B, N, 3, H, d), torch.bfloat16)
+    for i, name in enumerate(("dq", "dk", "dv")):
+        kw = {name: meta.unbind(2)[i]}
+        with pytest.raises(ValueError, match=f"^{name} must be on"):
+            aa.fa_bwd(q, k, v, o, lse, do, **kw)
+    with pytest.raises(TypeError, match="^dk must be"):
+        aa.fa_bwd(q, k, v, o, lse, do, dk=torch.zeros(B, N, H, d, dtype=torch.float16))
+
+
+def test_attention_qkvpacked_argument_checks():
+    torch = pytest.importorskip("torch")
+    x4 = torch.zeros(10, 3, 2, 64, dtype=torch.bfloat16)
+    x5 = torch.zeros(1, 10, 3, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="qkv must be a"):
+        aa.attention_qkvpacked(x4)                                  # varlen layout without cu_seqlens
+    with pytest.raises(ValueError, match="qkv must be a"):
+        aa.attention_qkvpacked(x5, cu_seqlens=cu, max_seqlen=10)    # dense layout with cu_seqlens
+    with pytest.raises(ValueError, match="qkv must be a"):
+        aa.attention_qkvpacked(torch.zeros(1, 10, 4, 2, 64))        # not three tensors
+    with pytest.raises(ValueError, match="max_seqlen"):
+        aa.attention_qkvpacked(x4, cu_seqlens=cu)
+
+
+def test_kernel_view_keeps_readable_views_and_copies_the_rest():
+    """Views the strided entry points read in place are passed as they are; others are copied."""
+    torch = pytest.importorskip("torch")
+    packed = torch.zeros(2, 33, 3, 4, 64, dtype=torch.bfloat16)
+    q = packed.unbind(2)[0]                                         # token stride 3*4*64, head stride 64
+    assert aa._kernel_view(q).data_ptr() == q.data_ptr()
+    assert aa._kernel_view(packed, token_dim=-4).data_ptr() == packed.data_ptr()
+    bhsd = torch.zeros(2, 4, 33, 64, dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    assert aa._kernel_view(bhsd).data_ptr() == bhsd.data_ptr()      # head stride 33*64
+    ones = torch.ones(64, dtype=torch.bfloat16).expand(2, 33, 4, 64)
+    assert aa._kernel_view(ones).data_ptr() == ones.data_ptr()      # zero strides are readable
+    col = torch.zeros(2, 33, 4, 64, dtype=torch.bfloat16).transpose(-1, -2).contiguous().transpose(-1, -2)
+    out = aa._kernel_view(col)                                      # d not contiguous
+    assert out.is_contiguous() and out.data_ptr() != col.data_ptr()
+    odd = torch.zeros(2, 33, 4, 68, dtype=torch.bfloat16)[..., :64]  # token stride 272, head 68
+    out = aa._kernel_view(odd)                                      # 68 is not a multiple of 8
+    assert out.is_contiguous() and out.data_ptr() != odd.data_ptr()
