@@ -7,22 +7,29 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = dO_i . O_i,
 //   dQ = scale dS K,   dK = scale dS^T Q.
 // Three kernels, run in this order on one stream:
-//   * delta_kernel: D_i = sum_e dO_ie O_ie in fp32, one row per lane;
+//   * delta_kernel: D_i = sum_e dO_ie O_ie in fp32, d/8 lanes per row;
 //   * dkdv_kernel:  one workgroup per 128 keys of one (batch or sequence,
-//     head); each lane owns one key, with its K and V rows in VGPRs; 64-query
-//     tiles of Q and dO stream through LDS. Per tile: S = Q K^T and
+//     head); each lane owns one key, with its K and V rows in registers;
+//     64-query tiles of Q and dO stream through LDS. Per tile: S = Q K^T and
 //     dP = dO V^T on the matrix cores (keys in the accumulator columns), P and
 //     dS in registers, then dV^T += dO^T P and dK^T += Q^T dS, whose A
-//     operands are transposing LDS reads of the same Q and dO tiles;
+//     operands are transposing LDS reads of the same Q and dO tiles. At
+//     d = 256 two workgroups share a key tile, each accumulating dK and dV
+//     for one half of the head dimension (S and dP over the full d);
 //   * dq_kernel:    one workgroup per 128 queries; each lane owns one query
-//     (Q and dO rows in VGPRs, L and D lane-local); 64-key tiles of K and V
-//     stream through LDS. Per tile: S^T = K Q^T and dP^T = V dO^T, dS^T in
+//     (Q and dO rows in registers, L and D lane-local); 64-key tiles of K and
+//     V stream through LDS. Per tile: S^T = K Q^T and dP^T = V dO^T, dS^T in
 //     registers, then dQ^T += K^T dS^T (A operand: transposing reads of K).
-//     Its state fits 256 registers at every d, so two workgroups share a CU
-//     (two waves per SIMD: one wave's exponentials overlap the other's
+//     Up to d = 128 its state fits 256 registers, so two workgroups share a
+//     CU (two waves per SIMD: one wave's exponentials overlap the other's
 //     products); the dK/dV kernel does the same where it fits (kDkdvWaves).
+//     Where a kernel runs one wave per SIMD, its LDS operands are read
+//     several products ahead through a register ring.
 // dQ is produced by its own pass over the keys (S and dP recomputed once more)
 // instead of by atomic adds, so the library needs no accumulation buffer.
+// The translation unit is compiled with MFMA results in the arch VGPRs
+// (-amdgpu-mfma-vgpr-form): in the AGPR form the one-wave-per-SIMD dK/dV
+// loop moved its accumulators between register files every tile.
 //
 // Operand layouts are those of the forward (v_mfma_f32_32x32x16, wave64):
 // accumulator lane l, register r holds D[8(r/4) + 4(l/32) + r%4][l%32], and
@@ -94,8 +101,8 @@ constexpr float kLog2eF = 1.44269504088896340736f;
 // Waves per SIMD of the dK/dV kernel: two workgroups share a CU (two waves
 // per SIMD, so one wave's exponentials overlap the other's products) where
 // the per-lane state fits in 256 registers without spilling: d = 32, and
-// d = 64 except the local pattern. At d = 128 one wave holds its K, V rows
-// and both accumulators in up to 512 registers.
+// d = 64 except the local pattern. At d = 128 and 256 one wave holds its K,
+// V rows and both accumulators in up to 512 registers.
 template <int D, bool LOCAL>
 constexpr int kDkdvWaves = (D == 32 || (D == 64 && !LOCAL)) ? 2 : 1;
 // LDS operand reads the dK/dV kernel keeps in flight ahead of its products
