@@ -96,6 +96,12 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;   // rows a workgroup owns
 constexpr int kBwdTile = 64;               // rows of a streamed LDS tile
+// Bytes of padding after each row of a streamed LDS tile: 16, and 32 at
+// d = 256, where the wider padding spreads the transposing reads over the
+// banks (measured at d = 256: +5 % on the backward; at d = 128 it changed
+// nothing but cost the dQ kernel a small spill).
+template <int D>
+constexpr int kRowPad = D == 256 ? 32 : 16;
 constexpr int kReadAhead = 4;              // LDS operand reads in flight ahead of the products (dQ)
 constexpr float kLog2eF = 1.44269504088896340736f;
 // Waves per SIMD of the dK/dV kernel: two workgroups share a CU (two waves
@@ -161,8 +167,9 @@ void delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ d
   if (row < nrows && c == 0) delta[((int64_t)b * H + h) * N + n] = acc;
 }
 
-// Row-major LDS tile of kBwdTile rows, each padded to 2 D + 16 bytes, i.e.
-// SL = D/8 + 1 slots of 16 bytes (slot D/8 of a row is padding). The tile's
+// Row-major LDS tile of kBwdTile rows, each padded to 2 D + kRowPad<D>
+// bytes, i.e. SL = D/8 + kRowPad<D>/16 slots of 16 bytes (the slots past D/8
+// are padding). The tile's
 // kBwdTile * SL slots are exactly SL blocks of 64 slots, so it is filled by
 // SL direct HBM -> LDS copies of 64 lanes (global_load_lds_dwordx4), split
 // over the workgroup's waves: lane l of copy i fills slot 64 i + l. Rows at
@@ -173,7 +180,7 @@ void delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ d
 template <int D>
 __device__ __forceinline__ void copy_tile_async(uint32_t lds_tile, const uint16_t* g, int rs,
                                                 int row0, int nvalid, int wave, int lane) {
-  constexpr int SL = D / 8 + 1;
+  constexpr int SL = D / 8 + kRowPad<D> / 16;
   const uint8_t* base = reinterpret_cast<const uint8_t*>(g + (int64_t)row0 * rs);
   const int last = nvalid - 1 - row0;        // last valid row of the tile, >= 0
 #pragma unroll
@@ -181,7 +188,7 @@ __device__ __forceinline__ void copy_tile_async(uint32_t lds_tile, const uint16_
     const int slot = 64 * i + lane;
     const int row = slot / SL, ch = slot % SL;
     const int r = row < last ? row : last;
-    const int c = ch < D / 8 ? ch : 0;        // the padding slot re-reads chunk 0
+    const int c = ch < D / 8 ? ch : 0;        // padding slots re-read chunk 0
     copy16_to_lds(base, (uint32_t)(r * 2 * rs + 16 * c), lds_tile + 1024 * i);
   }
 }
@@ -189,7 +196,7 @@ __device__ __forceinline__ void copy_tile_async(uint32_t lds_tile, const uint16_
 // Operand access of one lane into a padded tile (see the file comment).
 template <int D>
 struct BwdLanes {
-  static constexpr int RBP = 2 * D + 16;
+  static constexpr int RBP = 2 * D + kRowPad<D>;
   int row_rd;        // row-major A fragment: row l%32, 16 bytes at chunk 2 ds + l/32
   int tr_rd[D / 32]; // transposed A fragment of 32-column block b
   __device__ BwdLanes(int lane) {
@@ -357,7 +364,7 @@ void dkdv_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int RBP = 2 * D + 16;
+  constexpr int RBP = 2 * D + kRowPad<D>;
   constexpr int TB = kBwdTile * RBP;
   // [Q 0][dO 0][Q 1][dO 1][L 0][D 0][L 1][D 1]: buffer b holds the visited
   // query tiles b, b + 2, ...; L (times log2 e) and D per query of the tile.
@@ -691,7 +698,7 @@ void dq_kernel(BwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   static_assert(!(LOCAL && (BAND || KPM || VARLEN)), "mask combination");
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int RBP = 2 * D + 16;
+  constexpr int RBP = 2 * D + kRowPad<D>;
   constexpr int TB = kBwdTile * RBP;
   // [K 0][V 0][K 1][V 1]: buffer b holds the visited key tiles b, b + 2, ...
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];

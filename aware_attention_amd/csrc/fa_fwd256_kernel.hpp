@@ -41,7 +41,7 @@ void fwd256_kernel(FwdParams p) {
   static_assert(!(KPM && (BAND || VARLEN)) && !(CAUSAL && BAND), "mask combination");
   constexpr bool EMPTY_ROWS = BAND || KPM;
   constexpr int D = 256, DS = D / 16, DB = D / 32, BC = kBwdTile;
-  constexpr int RBP = 2 * D + 16;
+  constexpr int RBP = 2 * D + kRowPad<D>;
   constexpr int TB = BC * RBP;
   // [K 0][V 0][K 1][V 1]: buffer b holds key tile 2 m + b.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];

@@ -64,7 +64,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Wait until at most `newer` tiles' copies, issued after the tile that is
 // needed next, remain in flight. Each wave issues at least D/16 copies per
-// tile (K and V, kBwdWaves waves sharing D/8 + 1 slots per row), so allowing
+// tile (K and V, kBwdWaves waves sharing D/8 + kRowPad<D>/16 slots per row), so allowing
 // newer * D/16 outstanding never lets the needed tile's copies through
 // unfinished.
 template <int D, int R>
@@ -85,7 +85,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
                           amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 8)))
 void fwd_local_kernel(LocalParams p) {
   constexpr int DS = D / 16, DB = D / 32, BC = kBwdTile, R = kLocalRing<D>;
-  constexpr int RBP = 2 * D + 16;
+  constexpr int RBP = 2 * D + kRowPad<D>;
   constexpr int TB = BC * RBP;
   // [K 0][V 0][K 1][V 1]...: slot b holds visited tiles b, b + R, b + 2R, ...
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * R * TB];
