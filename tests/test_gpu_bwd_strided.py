@@ -63,9 +63,9 @@ def test_bwd_packed_qkv_dense(dtype, mask, d):
     gq, gk, gv, _ = attention_backward_dense(*f, scale, kw["causal"], window=kw["window"])
     tq, tk, _ = dense_terms(*f, scale, kw["causal"], EPS_O_HIP, window=kw["window"])
     what = f"packed {dtype} {mask} d={d}"
-    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
-    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
-    assert_grad_close(_np(dv), gv, "dv " + what)
+    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq, dtype=dtype)
+    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk, dtype=dtype)
+    assert_grad_close(_np(dv), gv, "dv " + what, dtype=dtype)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -109,9 +109,9 @@ def test_bwd_packed_qkv_varlen(dtype, mask):
                     qf[a:b, h], kf[a:b, h], vf[a:b, h], dof[a:b, h], scale, kw["causal"],
                     EPS_O_HIP, window=kw["window"])
     what = f"packed varlen {dtype} {mask}"
-    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq)
-    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk)
-    assert_grad_close(_np(dv), gv, "dv " + what)
+    assert_grad_close(_np(dq), gq, "dq " + what, extra=tq, dtype=dtype)
+    assert_grad_close(_np(dk), gk, "dk " + what, extra=tk, dtype=dtype)
+    assert_grad_close(_np(dv), gv, "dv " + what, dtype=dtype)
 
 
 def test_bwd_bhsd_layout_and_guarded_outputs():
