@@ -178,49 +178,76 @@ void fwd256_kernel(FwdParams p) {
       // when causal, outside the band, padding) get -inf, only on the tiles
       // that can hold them.
       const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0) || BAND || KPM;
-      float mt = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          bool ok = (key < Nk) & (!CAUSAL | (key <= qrow));
-          if constexpr (BAND) ok = ok & (key >= qrow + band_lo) & (key <= qrow + band_hi);
-          if constexpr (KPM) ok = ok & (((kvalid >> (16 * kb + r)) & 1u) != 0);
-          ok = ok | !masked;
-          s[kb][r] = ok ? s[kb][r] * s2 : kNegInf;
-          mt = fmaxf(mt, s[kb][r]);
-        }
-      }
-      mt = max_xor32(mt);
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
-        asm volatile("" ::: "memory");   // keep the rescale a real branch
-        const float m_new = fmaxf(m_run, mt);
-        // A row that has seen no key yet keeps m = -inf (no NaN from -inf - -inf).
-        const float alpha = (EMPTY_ROWS && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) o[b] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (EMPTY_ROWS && m_run == kNegInf) ? 0.f : m_run;   // no key yet: p = 0
       bf16x8 pb[2][2];
+      // P~ = exp2(x - m) into the MFMA operands pb; returns the lane's sum.
+      // x = S^T scale_log2, or the already scaled and masked s.
+      auto exps = [&](auto scaled_tag, float neg_m) __attribute__((always_inline)) -> float {
+        constexpr bool scaled = decltype(scaled_tag)::value;
+        float sum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
+          for (int t = 0; t < 2; ++t) {
+            u32x4 w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * t + 2 * i;
-            const float e0 = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
-            const float e1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - m_use);
-            w[i] = pack2<F16>(e0, e1);
-            l_run += e0 + e1;
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * t + 2 * i;
+              const float x0 = scaled ? s[kb][r] + neg_m : __builtin_fmaf(s[kb][r], s2, neg_m);
+              const float x1 = scaled ? s[kb][r + 1] + neg_m : __builtin_fmaf(s[kb][r + 1], s2, neg_m);
+              const float e0 = __builtin_amdgcn_exp2f(x0);
+              const float e1 = __builtin_amdgcn_exp2f(x1);
+              w[i] = pack2<F16>(e0, e1);
+              sum += e0 + e1;
+            }
+            pb[kb][t] = __builtin_bit_cast(bf16x8, w);
           }
-          pb[kb][t] = __builtin_bit_cast(bf16x8, w);
         }
+        return sum;
+      };
+      // Unmasked tile: exponentials against the current offset first; the
+      // lane's sum bounds each of its P~, so the row maximum and the rescale
+      // below are needed only when some lane's sum exceeds 2^kRescaleTau (or
+      // is not a number; the first tile of a row has m = -inf and always
+      // takes that path). Masked tiles take it always.
+      float tsum = 0.f;
+      bool full = true;
+      if (!EMPTY_ROWS && !masked) {
+        tsum = exps(std::false_type{}, -m_run);
+        full = __builtin_amdgcn_ballot_w64(!(tsum <= (float)(1 << (int)kRescaleTau))) != 0;
       }
+      if (full) {
+        // A real branch, and m_run opaque, so the exponentials above are
+        // not kept alive for reuse.
+        asm volatile("" : "+v"(m_run) : : "memory");
+        float mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+            bool ok = (key < Nk) & (!CAUSAL | (key <= qrow));
+            if constexpr (BAND) ok = ok & (key >= qrow + band_lo) & (key <= qrow + band_hi);
+            if constexpr (KPM) ok = ok & (((kvalid >> (16 * kb + r)) & 1u) != 0);
+            ok = ok | !masked;
+            s[kb][r] = ok ? s[kb][r] * s2 : kNegInf;
+            mt = fmaxf(mt, s[kb][r]);
+          }
+        }
+        mt = max_xor32(mt);
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
+          asm volatile("" ::: "memory");   // keep the rescale a real branch
+          const float m_new = fmaxf(m_run, mt);
+          // A row that has seen no key yet keeps m = -inf (no NaN from -inf - -inf).
+          const float alpha = (EMPTY_ROWS && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int b = 0; b < DB; ++b) o[b] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = (EMPTY_ROWS && m_run == kNegInf) ? 0.f : m_run;   // no key yet: p = 0
+        tsum = exps(std::true_type{}, -m_use);
+      }
+      l_run += tsum;
       // O^T += V^T P^T, with the same read-ahead for the transposed V
       // operands (steps st = (16-key group g = st / DB, column block st % DB)).
       constexpr int NP = 4 * DB;

@@ -614,6 +614,39 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
+  // P~ = exp2(S^T scale_log2 - m) of one tile into the MFMA operands pb,
+  // returning this lane's sum of P~ (masked tiles: s already scaled, masked
+  // scores -inf).
+  auto exps = [&](auto masked_tag, float neg_m) __attribute__((always_inline)) -> float {
+    constexpr bool masked = decltype(masked_tag)::value;
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * t + 2 * i;
+          float x0, x1;
+          if constexpr (masked) {
+            x0 = s[kb][r] + neg_m;
+            x1 = s[kb][r + 1] + neg_m;
+          } else {
+            x0 = __builtin_fmaf(s[kb][r], s2, neg_m);
+            x1 = __builtin_fmaf(s[kb][r + 1], s2, neg_m);
+          }
+          const float e0 = __builtin_amdgcn_exp2f(x0);
+          const float e1 = __builtin_amdgcn_exp2f(x1);
+          w[i] = pack2<F16>(e0, e1);
+          sum += e0 + e1;
+        }
+        pb[kb][t] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    return sum;
+  };
+
   // Online softmax of one tile: s -> pb, updating m_run, l_run and (rarely) o.
   // Instantiated separately for tiles that need the mask and tiles that do
   // not, so the common path carries no per-element selects.
@@ -658,30 +691,50 @@ void fwd_kernel(FwdParams p) {
     // A row that has seen no key yet (band only) keeps m = -inf; its
     // exponentials are of -inf and must come out 0, not NaN.
     const float neg_m = (EMPTY_ROWS && m_run == kNegInf) ? 0.f : -m_run;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 8 * t + 2 * i;
-          float x0, x1;
-          if constexpr (masked) {
-            x0 = s[kb][r] + neg_m;
-            x1 = s[kb][r + 1] + neg_m;
-          } else {
-            x0 = __builtin_fmaf(s[kb][r], s2, neg_m);
-            x1 = __builtin_fmaf(s[kb][r + 1], s2, neg_m);
-          }
-          const float e0 = __builtin_amdgcn_exp2f(x0);
-          const float e1 = __builtin_amdgcn_exp2f(x1);
-          w[i] = pack2<F16>(e0, e1);
-          l_run += e0 + e1;
-        }
-        pb[kb][t] = __builtin_bit_cast(bf16x8, w);
-      }
+    l_run += exps(masked_tag, neg_m);
+  };
+
+  // Softmax of a full unmasked tile in the steady loop, without the row
+  // maximum. The exponentials are taken against the current offset m_run
+  // straight away; the lane's sum of the tile's P~ then bounds every one of
+  // its terms (they are non-negative), so a sum of at most 2^kRescaleTau
+  // proves that no P~ of the lane exceeds 2^kRescaleTau, which is all the
+  // deferred rescale guarantees. Only when some lane's sum is larger (or not
+  // a number) does the wave take the full path above: the row maximum, the
+  // rescale if the maximum moved by more than kRescaleTau, and the
+  // exponentials again. Once a row's offset is set this happens on a
+  // vanishing fraction of tiles, and the common tile saves the maximum's
+  // 16 v_max3, the exchange and the compare.
+  auto softmax_lazy = [&]() __attribute__((always_inline)) {
+    // A wave whose rows have no offset yet (their first tile) goes straight
+    // to the full path.
+    float tsum = 0.f;
+    bool full = true;
+    if (__builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0) {
+      tsum = exps(std::false_type{}, -m_run);
+      full = __builtin_amdgcn_ballot_w64(!(tsum <= (float)(1 << (int)kRescaleTau))) != 0;
     }
+    if (full) {
+      // A real branch, not selects; m_run made opaque, or the compiler keeps
+      // the exponentials above alive to reuse them below.
+      asm volatile("" : "+v"(m_run) : : "memory");
+      float mt = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt = max3(mt, s[kb][r], s[kb][r + 1]);
+      }
+      mt = max_xor32(mt * s2);
+      // The offset moves to the row maximum (alpha = 1 if it did not grow).
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      m_run = m_new;
+      tsum = exps(std::false_type{}, -m_run);
+    }
+    l_run += tsum;
   };
 
   // Key padding mask of a tile: lane l reads the byte of key 64 kt + l, and a
@@ -824,11 +877,11 @@ void fwd_kernel(FwdParams p) {
           for (int n = 0; n < NPW; ++n) copy16_to_lds(gv, (uint32_t)v_src[n], lv + n * 1024);
         });
         stress_pause(4 * j + 1);
-        softmax_tile(std::false_type{}, 0, 0u);
+        softmax_lazy();
         stress_pause(4 * j + 2);
         __builtin_amdgcn_s_waitcnt(0);   // this period's copies have landed
       } else {
-        softmax_tile(std::false_type{}, 0, 0u);
+        softmax_lazy();
         stress_pause(4 * j + 1);
         qk_pv(j, [] {});
       }

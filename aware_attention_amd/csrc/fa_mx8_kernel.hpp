@@ -311,6 +311,37 @@ void fwd_mx8_kernel(Mx8Params p) {
     else if (do_pv) qk_pv(std::false_type{}, std::true_type{}, kt);
   };
 
+  // P~ = exp2(x - m) of one tile, rounded to E4M3 and regrouped across the
+  // lane halves into the B operand pb; returns this lane's sum of P~ (x =
+  // S^T scale_log2, or the already scaled, masked s).
+  auto exps = [&](auto masked_tag, float neg_m) __attribute__((always_inline)) -> float {
+    constexpr bool masked = decltype(masked_tag)::value;
+    float sum = 0.f;
+    uint32_t w[KB][4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          e[j] = __builtin_amdgcn_exp2f(masked ? s[kb][r] + neg_m : __builtin_fmaf(s[kb][r], s2, neg_m));
+        }
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
+        w[kb][g] = (uint32_t)x;
+        sum += (e[0] + e[1]) + (e[2] + e[3]);
+      }
+      // lane half h then holds keys 16 h + 0..15 of the block, in order
+      swap32(w[kb][0], w[kb][2]);
+      swap32(w[kb][1], w[kb][3]);
+    }
+    pb = i32x8{(int)w[0][0], (int)w[0][2], (int)w[0][1], (int)w[0][3],
+               (int)w[1][0], (int)w[1][2], (int)w[1][1], (int)w[1][3]};
+    return sum;
+  };
+
   // Online softmax of one tile (fwd_kernel's, with P~ rounded to E4M3 and
   // regrouped across the lane halves for the B operand).
   auto softmax_tile = [&](auto masked_tag, int k0) __attribute__((always_inline)) {
@@ -345,29 +376,42 @@ void fwd_mx8_kernel(Mx8Params p) {
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
       m_run = m_new;
     }
-    const float neg_m = -m_run;
-    uint32_t w[KB][4];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float e[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          e[j] = __builtin_amdgcn_exp2f(masked ? s[kb][r] + neg_m : __builtin_fmaf(s[kb][r], s2, neg_m));
-        }
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
-        w[kb][g] = (uint32_t)x;
-        l_run += (e[0] + e[1]) + (e[2] + e[3]);
-      }
-      // lane half h then holds keys 16 h + 0..15 of the block, in order
-      swap32(w[kb][0], w[kb][2]);
-      swap32(w[kb][1], w[kb][3]);
+    l_run += exps(masked_tag, -m_run);
+  };
+
+  // Softmax of a full unmasked tile in the steady loop, without the row
+  // maximum (fwd_kernel's): exponentials against the current offset first;
+  // the lane's sum of P~ bounds each of its terms, so only a sum above
+  // 2^kRescaleTau (or not a number) makes the wave take the maximum, the
+  // rescale and the exponentials again. P~ <= 2^kRescaleTau stays below
+  // E4M3's largest finite value either way.
+  auto softmax_lazy = [&]() __attribute__((always_inline)) {
+    // A wave whose rows have no offset yet (their first tile) goes straight
+    // to the full path.
+    float tsum = 0.f;
+    bool full = true;
+    if (__builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0) {
+      tsum = exps(std::false_type{}, -m_run);
+      full = __builtin_amdgcn_ballot_w64(!(tsum <= (float)(1 << (int)kRescaleTau))) != 0;
     }
-    pb = i32x8{(int)w[0][0], (int)w[0][2], (int)w[0][1], (int)w[0][3],
-               (int)w[1][0], (int)w[1][2], (int)w[1][1], (int)w[1][3]};
+    if (full) {
+      asm volatile("" : "+v"(m_run) : : "memory");   // a real branch; no reuse of the above
+      float mt = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt = max3(mt, s[kb][r], s[kb][r + 1]);
+      }
+      mt = max_xor32(mt * s2);
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      m_run = m_new;
+      tsum = exps(std::false_type{}, -m_run);
+    }
+    l_run += tsum;
   };
   auto softmax = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
@@ -420,11 +464,11 @@ void fwd_mx8_kernel(Mx8Params p) {
       copy_v(j);
       qk_pv(std::true_type{}, std::true_type{}, j);
       stress_pause(4 * j + 1);
-      softmax_tile(std::false_type{}, 0);
+      softmax_lazy();
       stress_pause(4 * j + 2);
       __builtin_amdgcn_s_waitcnt(0);
     } else {
-      softmax_tile(std::false_type{}, 0);
+      softmax_lazy();
       stress_pause(4 * j + 1);
       qk_pv(std::true_type{}, std::true_type{}, j);
     }
