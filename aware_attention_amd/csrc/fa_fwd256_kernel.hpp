@@ -149,11 +149,14 @@ void fwd256_kernel(FwdParams p) {
     const uint8_t* v_lds = smem + (2 * buf + 1) * TB;
     if (wave_has && kt >= wave_first_kt && kt <= wave_last_kt) {
       uint32_t kvalid = ~0u;   // padding mask: validity bits of this lane's 32 keys
+      bool kall = true;        // ... and whether all 64 keys of the tile are valid
       if constexpr (KPM) {
         const int key = k0 + lane;
         const bool kv = span.run ? (key >= span.lo && key <= span.hi)
                                  : (key < Nk && kpm_row[key] != 0);
-        kvalid = gather_lane_bits(__builtin_amdgcn_ballot_w64(kv), hi);
+        const uint64_t kbits = __builtin_amdgcn_ballot_w64(kv);
+        kvalid = gather_lane_bits(kbits, hi);
+        kall = kbits == ~0ull;
       }
       // S^T = K Q^T: 64 keys x the wave's 32 queries, keys in accumulator rows.
       // With one wave per SIMD nothing else hides the LDS latency: the K
@@ -177,7 +180,11 @@ void fwd256_kernel(FwdParams p) {
       // Online softmax (base 2); masked keys (past the end, after the query
       // when causal, outside the band, padding) get -inf, only on the tiles
       // that can hold them.
-      const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0) || BAND || KPM;
+      // Masked: some (row, key) pair of the wave's rows and the tile's keys is
+      // hidden (past the end, after the query, outside the band, padding).
+      const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0) ||
+                          (BAND && (k0 < qw1 + band_lo || k0 + BC - 1 > qw0 + band_hi)) ||
+                          (KPM && !kall);
       bf16x8 pb[2][2];
       // P~ = exp2(x - m) into the MFMA operands pb; returns the lane's sum.
       // x = S^T scale_log2, or the already scaled and masked s.
@@ -207,11 +214,11 @@ void fwd256_kernel(FwdParams p) {
       // Unmasked tile: exponentials against the current offset first; the
       // lane's sum bounds each of its P~, so the row maximum and the rescale
       // below are needed only when some lane's sum exceeds 2^kRescaleTau (or
-      // is not a number; the first tile of a row has m = -inf and always
-      // takes that path). Masked tiles take it always.
+      // is not a number). Masked tiles, and a wave with a row that has no
+      // offset yet (its first visible tile), take that path always.
       float tsum = 0.f;
       bool full = true;
-      if (!EMPTY_ROWS && !masked) {
+      if (!masked && __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0) {
         tsum = exps(std::false_type{}, -m_run);
         full = __builtin_amdgcn_ballot_w64(!(tsum <= (float)(1 << (int)kRescaleTau))) != 0;
       }
