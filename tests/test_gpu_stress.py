@@ -18,7 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 STRESS_LIB = os.path.join(ROOT, "aware_attention_amd", "libfa_stress.so")
 SUITE = ["tests/test_gpu_parity.py", "tests/test_gpu_band.py", "tests/test_gpu_mx8.py",
          "tests/test_gpu_backward.py", "tests/test_gpu_local.py", "tests/test_gpu_d256.py",
-         "tests/test_gpu_padded.py", "tests/test_gpu_general.py", "tests/test_gpu_decode.py"]
+         "tests/test_gpu_padded.py", "tests/test_gpu_general.py", "tests/test_gpu_decode.py",
+         "tests/test_gpu_rescale.py"]
 
 
 def test_parity_suite_under_timing_jitter():
