@@ -214,69 +214,98 @@ void fwd_local_kernel(LocalParams p) {
         for (int kb = 0; kb < 2; ++kb)
           s[kb] = mfma32<F16>(lds16(k_lds, kb * 32 * RBP + ln.row_rd + ds * 32), qr[ds], s[kb]);
       }
-      // Visibility of each score: an anchor query sees every key (up to
-      // itself when causal); a map query decides from the keys' map positions.
-      float mt = kNegInf;
-      if (anchor_wg) {
+      // P~ = exp2(x - m) into the MFMA operands pb; returns the lane's sum.
+      // x = S^T scale_log2, or the already scaled and masked s.
+      bf16x8 pb[2][2];
+      auto exps = [&](auto scaled_tag, float neg_m) __attribute__((always_inline)) -> float {
+        constexpr bool scaled = decltype(scaled_tag)::value;
+        float sum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool vis = (key < N) & (!CAUSAL | (key <= qrow));
-            s[kb][r] = vis ? s[kb][r] * s2 : kNegInf;
-            mt = fmaxf(mt, s[kb][r]);
+          for (int t = 0; t < 2; ++t) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * t + 2 * i;
+              const float x0 = scaled ? s[kb][r] + neg_m : __builtin_fmaf(s[kb][r], s2, neg_m);
+              const float x1 = scaled ? s[kb][r + 1] + neg_m : __builtin_fmaf(s[kb][r + 1], s2, neg_m);
+              const float e0 = __builtin_amdgcn_exp2f(x0);
+              const float e1 = __builtin_amdgcn_exp2f(x1);
+              w[i] = pack2<F16>(e0, e1);
+              sum += e0 + e1;
+            }
+            pb[kb][t] = __builtin_bit_cast(bf16x8, w);
           }
         }
-      } else {
+        return sum;
+      };
+      // An anchor query sees every key of a tile inside the sequence (when
+      // causal, of a tile left of the wave's first row): no mask. Such a tile
+      // is exponentiated against the current offset first; the lane's sum of
+      // P~ bounds each term, so the row maximum and the rescale are needed
+      // only when some lane's sum exceeds 2^kRescaleTau (or is not a number),
+      // or while a row has no offset yet.
+      const bool open_tile = anchor_wg && k0 + BC <= N && (!CAUSAL || k0 + BC - 1 <= qw0);
+      float tsum = 0.f;
+      bool full = true;
+      if (open_tile && __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0) {
+        tsum = exps(std::false_type{}, -m_run);
+        full = __builtin_amdgcn_ballot_w64(!(tsum <= (float)(1 << (int)kRescaleTau))) != 0;
+      }
+      if (full) {
+        // A real branch, and m_run opaque, so the exponentials above are not
+        // kept alive for reuse.
+        asm volatile("" : "+v"(m_run) : : "memory");
+        // Visibility of each score: an anchor query sees every key (up to
+        // itself when causal); a map query decides from the keys' map positions.
+        float mt = kNegInf;
+        if (anchor_wg) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int kk = 32 * kb + 8 * g + 4 * hi;   // first of this lane's 4 keys
-            const i32x4 kr = *reinterpret_cast<const i32x4*>(&kmrow[buf][kk]);
-            const i32x4 kc = *reinterpret_cast<const i32x4*>(&kmcol[buf][kk]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              // Bitwise, not short-circuit, operators: one select per score
-              // instead of divergent branches.
-              bool vis = map_near(kr[e], kc[e], ir, ic, WR, WC) | (kr[e] == kKeyAnchor);
-              if (CAUSAL) vis = vis & (k0 + kk + e <= qrow);
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+              const bool vis = (key < N) & (!CAUSAL | (key <= qrow));
               s[kb][r] = vis ? s[kb][r] * s2 : kNegInf;
               mt = fmaxf(mt, s[kb][r]);
             }
           }
-        }
-      }
-      mt = max_xor32(mt);
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
-        asm volatile("" ::: "memory");   // keep the rescale a real branch
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
+        } else {
 #pragma unroll
-        for (int b = 0; b < DB; ++b) o[b] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == kNegInf ? 0.f : m_run;   // no key seen yet: every p is 0
-      bf16x8 pb[2][2];
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+            for (int g = 0; g < 4; ++g) {
+              const int kk = 32 * kb + 8 * g + 4 * hi;   // first of this lane's 4 keys
+              const i32x4 kr = *reinterpret_cast<const i32x4*>(&kmrow[buf][kk]);
+              const i32x4 kc = *reinterpret_cast<const i32x4*>(&kmcol[buf][kk]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * t + 2 * i;
-            const float e0 = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
-            const float e1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - m_use);
-            w[i] = pack2<F16>(e0, e1);
-            l_run += e0 + e1;
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                // Bitwise, not short-circuit, operators: one select per score
+                // instead of divergent branches.
+                bool vis = map_near(kr[e], kc[e], ir, ic, WR, WC) | (kr[e] == kKeyAnchor);
+                if (CAUSAL) vis = vis & (k0 + kk + e <= qrow);
+                s[kb][r] = vis ? s[kb][r] * s2 : kNegInf;
+                mt = fmaxf(mt, s[kb][r]);
+              }
+            }
           }
-          pb[kb][t] = __builtin_bit_cast(bf16x8, w);
         }
+        mt = max_xor32(mt);
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleTau) != 0) {
+          asm volatile("" ::: "memory");   // keep the rescale a real branch
+          const float m_new = fmaxf(m_run, mt);
+          const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int b = 0; b < DB; ++b) o[b] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = m_run == kNegInf ? 0.f : m_run;   // no key seen yet: every p is 0
+        tsum = exps(std::true_type{}, -m_use);
       }
+      l_run += tsum;
       // O^T += V^T P^T.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
