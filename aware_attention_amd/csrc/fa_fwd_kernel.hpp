@@ -578,7 +578,10 @@ void fwd_kernel(FwdParams p) {
   auto qk_pv = [&](int kt, auto&& between) __attribute__((always_inline)) {
     constexpr int N = KB * DS;                   // MFMAs per product
     static_assert(N == DB * KB * 2, "both products have the same length");
-    constexpr int R = 2 * N < kPrefetch ? 2 * N : kPrefetch;
+    // Causal d = 128 has registers to spare (221 of 256 with 8): a 16-deep
+    // ring there (253, no spills) measured +1.9 % on the causal prefill shape.
+    constexpr int PF = CAUSAL && D == 128 ? 2 * kPrefetch : kPrefetch;
+    constexpr int R = 2 * N < PF ? 2 * N : PF;
     const int kbase = (kt & 1) * TILE_BYTES;
     const int vbase = (2 + ((kt - 1) & 1)) * TILE_BYTES;
     auto frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
