@@ -895,23 +895,42 @@ void fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
+  // A lane holds 4-element pieces of its row scattered over d, so storing
+  // them directly takes 16 eight-byte stores per lane, each instruction
+  // touching 32 rows. Instead each wave transposes its 32 x D tile of O
+  // through its own 32 * 2D bytes of the K/V buffers, free once every wave
+  // has crossed the last barrier (a workgroup without key tiles never wrote
+  // them), and then stores whole rows: 16 bytes per lane, D/8 lanes per row.
+  // The 16-byte chunks of a row are XOR-swizzled by the row's position in
+  // the 64 LDS banks, so both the writes and the reads spread over the banks.
   const float l_tot = l_run + xor32(l_run);
-  if (qrow < Nq) {
-    const bool empty = (EMPTY_ROWS && l_tot == 0.f) || !q_valid;
-    const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(l_tot);
-    uint16_t* orow = p.o + o_off + (int64_t)qrow * o_ts;
+  const bool empty = (EMPTY_ROWS && l_tot == 0.f) || !q_valid;
+  const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(l_tot);
+  constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  auto oswz = [](int r) { return (r * RB / 256) % CPR; };
+  uint8_t* wtile = smem + wave * 32 * RB;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+  for (int b = 0; b < DB; ++b) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 w = {pack2<F16>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv),
-                         pack2<F16>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
-        *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g + 4 * hi) = w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      const uint2 w = {pack2<F16>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv),
+                       pack2<F16>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
+      const int c = 4 * b + g;                        // chunk of d = 32b + 8g + 4hi .. +3
+      *reinterpret_cast<uint2*>(wtile + l32 * RB + ((c ^ oswz(l32)) * 16) + 8 * hi) = w;
     }
-    if (hi == 0)
-      p.lse[l_off + qrow] = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's tile is in LDS
+  constexpr int RPI = 64 / CPR;                       // rows per store instruction
+  const int rsub = lane / CPR, ch = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + rsub;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(wtile + r * RB + ((ch ^ oswz(r)) * 16));
+    if (qw0 + r < Nq)
+      *reinterpret_cast<u32x4*>(p.o + o_off + (int64_t)(qw0 + r) * o_ts + 8 * ch) = val;
+  }
+  if (qrow < Nq && hi == 0)
+    p.lse[l_off + qrow] = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace fa
