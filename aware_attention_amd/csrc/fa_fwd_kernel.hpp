@@ -219,6 +219,46 @@ __device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, 
       : "memory", "m0");
 }
 
+// Store a wave's 32 x D block of rows held transposed in MFMA accumulators
+// (lane l owns row l % 32; register group b, g holds columns
+// 32 b + 8 g + 4 (l / 32) + 0..3), each row times its lane's `mul`, rounded to
+// the 16-bit element type. Stored directly, that is 16 eight-byte stores per
+// lane with every instruction touching 32 rows. Instead the block goes
+// through `wtile`, 32 * 2D bytes of LDS that this wave alone uses at this
+// point: the pieces are written with the 16-byte chunks of each row
+// XOR-swizzled by the row's position in the 64 LDS banks (so the writes and
+// the reads spread over the banks), read back in row order and stored as
+// whole rows, D/8 lanes per row and 16 bytes per lane. Rows r >= nrows are
+// not stored; row r goes to row0 + r * rstride (elements).
+template <int D, bool F16>
+__device__ __forceinline__ void store_tileT(uint16_t* row0, int64_t rstride, int nrows,
+                                            const f32x16 (&acc)[D / 32], float mul,
+                                            uint8_t* wtile, int lane) {
+  constexpr int RB = 2 * D, CPR = D / 8, RPI = 64 / CPR;
+  constexpr int RPB = RB < 256 ? 256 / RB : 1;        // rows per 256 bytes (64 banks)
+  constexpr int SW = CPR < 16 ? CPR : 16;
+  auto swz = [](int r) { return (r / RPB) % SW; };
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint2 w = {pack2<F16>(acc[b][4 * g] * mul, acc[b][4 * g + 1] * mul),
+                       pack2<F16>(acc[b][4 * g + 2] * mul, acc[b][4 * g + 3] * mul)};
+      const int c = 4 * b + g;                        // chunk of columns 8c .. 8c + 7
+      *reinterpret_cast<uint2*>(wtile + l32 * RB + ((c ^ swz(l32)) * 16) + 8 * hi) = w;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the block is in LDS
+  const int rsub = lane / CPR, ch = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + rsub;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(wtile + r * RB + ((ch ^ swz(r)) * 16));
+    if (r < nrows) *reinterpret_cast<u32x4*>(row0 + (int64_t)r * rstride + 8 * ch) = val;
+  }
+}
+
 // LDS tile layout shared by K and V: BC rows of D bf16 (2*D bytes), no
 // padding, 16-byte chunks permuted inside each row by an XOR with a
 // row-dependent mask so that the MFMA operand reads hit distinct LDS banks.
@@ -895,40 +935,14 @@ void fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = O_acc / l, L = ln2 * (m + log2 l) ----
-  // A lane holds 4-element pieces of its row scattered over d, so storing
-  // them directly takes 16 eight-byte stores per lane, each instruction
-  // touching 32 rows. Instead each wave transposes its 32 x D tile of O
-  // through its own 32 * 2D bytes of the K/V buffers, free once every wave
-  // has crossed the last barrier (a workgroup without key tiles never wrote
-  // them), and then stores whole rows: 16 bytes per lane, D/8 lanes per row.
-  // The 16-byte chunks of a row are XOR-swizzled by the row's position in
-  // the 64 LDS banks, so both the writes and the reads spread over the banks.
+  // O goes out through LDS (store_tileT), each wave using its own 32 * 2D
+  // bytes of the K/V buffers, free once every wave has crossed the last
+  // barrier (a workgroup without key tiles never wrote them).
   const float l_tot = l_run + xor32(l_run);
   const bool empty = (EMPTY_ROWS && l_tot == 0.f) || !q_valid;
   const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(l_tot);
-  constexpr int CPR = D / 8;                          // 16-byte chunks per row
-  auto oswz = [](int r) { return (r * RB / 256) % CPR; };
-  uint8_t* wtile = smem + wave * 32 * RB;
-#pragma unroll
-  for (int b = 0; b < DB; ++b) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint2 w = {pack2<F16>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv),
-                       pack2<F16>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
-      const int c = 4 * b + g;                        // chunk of d = 32b + 8g + 4hi .. +3
-      *reinterpret_cast<uint2*>(wtile + l32 * RB + ((c ^ oswz(l32)) * 16) + 8 * hi) = w;
-    }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's tile is in LDS
-  constexpr int RPI = 64 / CPR;                       // rows per store instruction
-  const int rsub = lane / CPR, ch = lane % CPR;
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = i * RPI + rsub;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(wtile + r * RB + ((ch ^ oswz(r)) * 16));
-    if (qw0 + r < Nq)
-      *reinterpret_cast<u32x4*>(p.o + o_off + (int64_t)(qw0 + r) * o_ts + 8 * ch) = val;
-  }
+  store_tileT<D, F16>(p.o + o_off + (int64_t)qw0 * o_ts, o_ts, min(32, Nq - qw0), o, inv,
+                      smem + wave * 64 * D, lane);
   if (qrow < Nq && hi == 0)
     p.lse[l_off + qrow] = empty ? kNegInf : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }

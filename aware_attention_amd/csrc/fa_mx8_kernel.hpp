@@ -100,7 +100,11 @@ void fwd_mx8_kernel(Mx8Params p) {
   constexpr int KS = BC * (D / kMxBlock);    // K exponents of a tile
   constexpr int VS = (BC / kMxBlock) * D;    // V exponents of a tile
   constexpr int K0 = 0, V0 = 2 * KT, KS0 = 2 * KT + 2 * VT, VS0 = KS0 + 2 * KS;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (KT + VT + KS + VS)];
+  // Double-buffered tiles; the epilogue reuses the first kWaves * 32 * 2D
+  // bytes to transpose O (store_tileT).
+  constexpr int SMEM = 2 * (KT + VT + KS + VS) > kWaves * 64 * D ? 2 * (KT + VT + KS + VS)
+                                                                : kWaves * 64 * D;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x;
@@ -478,22 +482,15 @@ void fwd_mx8_kernel(Mx8Params p) {
   for (int j = js1; j <= n_kt; ++j) period(j);
 
   // ---- epilogue: O = O_acc / l, L = ln2 (m + log2 l) ----
+  // O goes out through LDS (store_tileT), each wave using its own 32 * 2D
+  // bytes, free once every wave has crossed the last barrier.
   const float l_tot = l_run + xor32(l_run);
-  if (qrow < Nq) {
-    const float inv = __builtin_amdgcn_rcpf(l_tot);
-    uint16_t* orow = p.o + ((int64_t)bidx * Nq + qrow) * tok + (int64_t)head * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 w = {pack2<false>(o[b][4 * g] * inv, o[b][4 * g + 1] * inv),
-                         pack2<false>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv)};
-        *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g + 4 * hi) = w;
-      }
-    }
-    if (hi == 0)
-      p.lse[((int64_t)bidx * p.H + head) * Nq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  }
+  if (qw0 < Nq)
+    store_tileT<D, false>(p.o + ((int64_t)bidx * Nq + qw0) * tok + (int64_t)head * D, tok,
+                          min(32, Nq - qw0), o, __builtin_amdgcn_rcpf(l_tot),
+                          smem + wave * 64 * D, lane);
+  if (qrow < Nq && hi == 0)
+    p.lse[((int64_t)bidx * p.H + head) * Nq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 // ---- quantisers (HBM-bound, one thread per 32-element block) ----
